@@ -1,0 +1,87 @@
+"""Plants plausible mistakes in a copy of the oracle source (on the CPU) and
+checks that the oracle's pins catch every one of them.
+
+Each mutant is one textual edit of oracle/oracle.c (a wrong index, a dropped
+term, a flipped sign, a transposed layout), compiled with gcc into a
+temporary library and run against the pin files in a child pytest process.
+A mutant that survives means the pins would not notice that mistake.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PINS = ["tests/test_oracle_formula.py", "tests/test_oracle_fp8.py",
+        "tests/test_oracle_attention.py"]
+
+# (name, original text, planted text, occurrence count expected)
+MUTANTS = [
+    ("size_drops_k_and_v", "return 2 * layers * kv_heads", "return layers * kv_heads"),
+    ("gqa_interleaved_heads", "int32_t h = hq / G;", "int32_t h = hq % Hkv;"),
+    ("slot_from_block_index", "int32_t slot = t % block_size;\n        double dot",
+     "int32_t slot = (t / block_size) % block_size;\n        double dot"),
+    ("table_column_off_by_one",
+     "block_tables[(int64_t)b * max_blocks + t / block_size];\n        int32_t slot = t % block_size;\n        double dot",
+     "block_tables[(int64_t)b * max_blocks + (t / block_size + 1) % ((t1 + block_size - 1) / block_size)];\n        int32_t slot = t % block_size;\n        double dot"),
+    ("pool_layout_transposed", "return (((int64_t)phys * bs + slot) * Hkv + h) * D + d;",
+     "return (((int64_t)phys * Hkv + h) * bs + slot) * D + d;"),
+    ("scale_dropped", "s[i] = scale * dot;", "s[i] = dot;"),
+    ("softmax_sign_flipped", "double w = exp(s[i] - m);", "double w = exp(m - s[i]);"),
+    ("no_normalisation", "out[d] /= l;", "out[d] /= 1.0;"),
+    ("lse_without_max", "lse = m + log(l);", "lse = log(l);"),
+    ("max_not_taken", "if (s[i] > m)\n            m = s[i];", "if (s[i] < m)\n            m = s[i];"),
+    ("e4m3_bias_8", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
+     "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3_subnormal_scale", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    ("ties_away_from_even", "c = (lo & 1) == 0 ? lo : hi;", "c = hi;"),
+    ("quantise_multiplies", "float y = x / scale;", "float y = x * scale;"),
+    ("no_saturation", "if (a >= 448.0)\n        return (uint8_t)(sign | 0x7E);",
+     "if (a >= 448.0)\n        return (uint8_t)(sign | 0x7F);"),
+    ("fp8_scale_ignores_head", "* (double)scales[(int64_t)phys * Hkv + h];",
+     "* (double)scales[(int64_t)phys * Hkv];"),
+    ("merge_weight_sign", "w = exp(lse_parts[s] - M);", "w = exp(M - lse_parts[s]);"),
+    ("merge_empty_as_lse_zero",
+     "if (lse_parts[s] == -INFINITY)\n            continue;\n        w = exp(lse_parts[s] - M);",
+     "w = lse_parts[s] == -INFINITY ? exp(-M) : exp(lse_parts[s] - M);"),
+    ("append_wrong_slot", "slot = t % block_size;\n        for (h = 0; h < Hkv; ++h) {",
+     "slot = (t + 1) % block_size;\n        for (h = 0; h < Hkv; ++h) {"),
+    ("append_swaps_k_v", "((uint16_t*)k_cache)[dst] = k_new[src];",
+     "((uint16_t*)k_cache)[dst] = v_new[src];"),
+    ("block_scale_amax_over_all_slots", "for (slot = 0; slot < live[p]; ++slot)",
+     "for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)"),
+    ("split_range_overlaps", "int32_t t0 = s * split_tokens;",
+     "int32_t t0 = s > 0 ? s * split_tokens - 1 : 0;"),
+]
+
+
+def _run_mutant(tmpdir, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"{name}: pattern not found"
+    mut = src.replace(old, new)
+    c_path = os.path.join(tmpdir, f"{name}.c")
+    so_path = os.path.join(tmpdir, f"{name}.so")
+    open(c_path, "w").write(mut)
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-w", "-o", so_path, c_path, "-lm"], check=True)
+    env = dict(os.environ, PKV_ORACLE_LIB=so_path)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PINS], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    return name, r.returncode
+
+
+def test_every_planted_mistake_is_caught(tmp_path):
+    with cf.ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        futs = [ex.submit(_run_mutant, str(tmp_path), *m) for m in MUTANTS]
+        results = [f.result() for f in futs]
+    survivors = [name for name, rc in results if rc == 0]
+    assert not survivors, f"pins did not catch: {survivors}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    name, rc = _run_mutant(str(tmp_path), "identity", "#include <math.h>", "#include <math.h>")
+    assert rc == 0
