@@ -1,0 +1,254 @@
+"""Throughput of one decode step of paged attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch: append the new
+token's K/V (paged_kv_append), split-context paged decode attention
+(paged_decode_attention) and the log-sum-exp merge (split_context_reduce).
+Inputs are seeded synthetic arrays already resident in HBM.
+
+Prints ONE JSON line.  value = KV-read GB/s of the whole step (ideal KV
+bytes 2 * sum(ctx) * Hkv * D * bytes_per_elem per step / step time).
+roofline = the attention kernel alone, timed with HIP events on the stream
+it is launched on.  cpu_baseline = the CPU oracle on a bounded sample of the
+same workload, on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved KV-read GB/s (% of HBM peak) + decode tokens/s, paged decode attn 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+# split_tokens used for each workload (0 = single pass)
+DEFAULT_SPLIT = {
+    "llama70b_b64_ragged1k_16k_bs32": 1024,
+    "llama70b_b4_ctx32k_split512_prefix2k": 512,
+    "llama8b_b32_ctx4096_bs16": 0,
+    "tiny_b4_hq8_hkv2_d64_bs16": 0,
+    "fp8_36layers_groups4_b32_ctx2k_8k": 0,
+}
+DEFAULT_WORKLOAD = "llama70b_b64_ragged1k_16k_bs32"
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--split", type=int, default=None, help="split_tokens (default per workload)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="measured HBM bytes per attention launch (written from rocprofv3)")
+    return p.parse_args()
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); "
+              "the decode kernel has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_273_amd as pkv
+    from synthetic import generate, make_workload
+
+    wl = make_workload(a.workload)
+    S = DEFAULT_SPLIT.get(wl.name, 0) if a.split is None else a.split
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    groups = [0] if wl.kv_dtype == "bf16" else [0]
+    inp = generate(wl, groups=groups)
+    print(f"bench: generated {wl.name} in {time.time() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            x = x.view(np.int16)
+        return torch.from_numpy(x).to(dev)
+
+    ks = vs = None
+    if wl.kv_dtype == "fp8":
+        # fp8 cache built on the device from the bf16 source values
+        # (input preparation only: amax / 448 per block and kv head)
+        def quant(src):
+            x = up(src).view(torch.bfloat16).float()
+            live = torch.from_numpy(
+                np.arange(wl.block_size)[None, :] < inp.live[:, None]).to(dev)
+            xm = torch.where(live[:, :, None, None] & torch.isfinite(x), x.abs(),
+                             torch.zeros_like(x))
+            amax = xm.amax(dim=(1, 3))
+            sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
+            y = (x / sc[:, None, :, None]).clamp(-448, 448)
+            return y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
+
+        k, ks = quant(inp.k_pool[0])
+        v, vs = quant(inp.v_pool[0])
+    else:
+        k, v = up(inp.k_pool[0]), up(inp.v_pool[0])
+    kn, vn = up(inp.k_new[0]), up(inp.v_new[0])
+    q = up(inp.query[0])
+    bt, cl = up(inp.block_tables), up(inp.context_lens)
+    ctx = inp.context_lens.astype(np.int64)
+    ideal = 2 * int(ctx.sum()) * wl.Hkv * wl.D * wl.bytes_per_elem
+    scale = float(inp.scale)
+
+    ms = pkv.max_splits_for(int(ctx.max()), S) if S else 1
+    out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    po = torch.empty((wl.B, wl.Hq, ms, wl.D), dtype=torch.float32, device=dev) if S else None
+    pl = torch.empty((wl.B, wl.Hq, ms), dtype=torch.float32, device=dev) if S else None
+
+    ev = []  # (start, end) around each attention launch in the timed region
+
+    def step(record):
+        pkv.paged_kv_append(kn, vn, k, v, bt, cl, k_scale=ks, v_scale=vs)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        if S:
+            pkv.paged_decode_attention(q, k, v, bt, cl, scale, split_tokens=S, partial_out=po,
+                                       partial_lse=pl, k_scale=ks, v_scale=vs)
+        else:
+            pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks, v_scale=vs)
+        if record:
+            e1.record()
+            ev.append((e0, e1))
+        if S:
+            pkv.split_context_reduce(po, pl, cl, S, out=out)
+
+    if a.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3 / len(ev)
+
+    step_s = wall / a.steps
+    gbs = ideal / step_s / 1e9
+    kern_gbs = ideal / kern_s / 1e9
+    traffic = None
+    try:
+        tj = json.load(open(a.traffic_json))
+        rec = tj.get(wl.name)
+        if rec and rec.get("split_tokens") == S:
+            traffic = rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = _cpu_baseline(inp, wl, a.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(wl.B / step_s, 1),
+        "config": {
+            "workload": wl.name, "batch": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
+            "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
+            "ctx_sum": int(ctx.sum()), "ctx_mean": round(float(ctx.mean()), 1),
+            "ctx_min": int(ctx.min()), "ctx_max": int(ctx.max()), "split_tokens": S,
+            "num_blocks": inp.num_blocks, "ideal_kv_bytes_per_step": ideal,
+            "step": "paged_kv_append + paged_decode_attention"
+                    + (" + split_context_reduce" if S else ""),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_kernel (paged_decode_attention)",
+            "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": ideal,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _cpu_baseline(inp, wl, target_s):
+    """The oracle (single-threaded C, fp64) on whole sequences of the same
+    workload until about target_s seconds of CPU time; GB/s on the same
+    ideal-byte formula."""
+    import numpy as np
+
+    import oracle
+
+    kp, vp = inp.k_pool[0], inp.v_pool[0]
+    kind = "bf16"
+    ks = vs = None
+    if wl.kv_dtype == "fp8":
+        ks = oracle.fp8_block_scales(kp, inp.block_tables, inp.context_lens, wl.block_size)
+        vs = oracle.fp8_block_scales(vp, inp.block_tables, inp.context_lens, wl.block_size)
+        kp, vp = oracle.fp8_quantize_pool(kp, ks), oracle.fp8_quantize_pool(vp, vs)
+        kind = "fp8"
+    oracle.append(inp.k_new[0], inp.v_new[0], kp, vp, inp.block_tables, inp.context_lens,
+                  wl.block_size, kv_dtype=kind, k_scale=ks, v_scale=vs)
+    done_bytes = 0
+    seqs = 0
+    t0 = time.perf_counter()
+    for b in range(wl.B):
+        sl = slice(b, b + 1)
+        oracle.paged_attention(np.ascontiguousarray(inp.query[0][sl]), kp, vp,
+                               np.ascontiguousarray(inp.block_tables[sl]),
+                               np.ascontiguousarray(inp.context_lens[sl]), inp.scale,
+                               block_size=wl.block_size, Hkv=wl.Hkv, kv_dtype=kind,
+                               k_scale=ks, v_scale=vs)
+        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * wl.bytes_per_elem
+        seqs += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    gbs = done_bytes / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{seqs} of {wl.B} sequences (all {wl.Hq} query heads, "
+                      f"{done_bytes / 1e6:.0f} MB of KV), single-threaded fp64 C, "
+                      f"{el:.1f} s; {seqs / el:.3f} sequences/s",
+            "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: decode-step attention over a paged
+ * KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [A] "KV-Cache Engineering: Paged Attention, Prefix Cache,
+ *        Disaggregation (2026)".
+ *   [B] "KV Cache Engineering: PagedAttention, Continuous Batching,
+ *        Attention Variants, and the Bandwidth Wall".
+ *   [C] "KV-Cache Engineering: The Memory Wall of LLM Serving".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Every tensor pointer is a DEVICE pointer (memory the caller allocated
+ *    on the GPU that is current when the call is made).  Tensors are
+ *    row-major and contiguous.  bf16 values travel as their uint16_t bit
+ *    patterns.  `stream` is a hipStream_t passed as void* (NULL = the
+ *    default stream).
+ *  * Ownership: the caller owns and allocates everything (pools, scales,
+ *    tables, lengths, partials, outputs).  The library allocates nothing,
+ *    frees nothing, never synchronises and keeps no state between calls;
+ *    each call only enqueues kernels on `stream` and returns.  Calls are
+ *    thread-safe.
+ *  * Errors: scalar arguments and pointer alignment are checked on the
+ *    host before anything is launched.  A bad argument returns
+ *    PKV_EINVAL, a shape outside the compiled kernel set returns
+ *    PKV_EUNSUPPORTED; nothing is launched in either case.  PKV_ELAUNCH
+ *    reports a launch failure (hipGetLastError).  Device-resident CONTENTS
+ *    (table entries, lengths) are preconditions, as for an OS page table,
+ *    and are not checked by the kernels: see "Table preconditions".
+ *
+ * Cache layout ([B] "PagedAttention": fixed-size physical blocks, any
+ * free block serves any sequence)
+ * ------------------------------------------------------------------
+ *  k_cache, v_cache : [num_blocks, block_size, Hkv, D]
+ *      kv_dtype PKV_BF16     : uint16_t bf16 bits
+ *      kv_dtype PKV_FP8_E4M3 : uint8_t OCP E4M3FN codes (max finite 448,
+ *                              0x7F/0xFF NaN, no infinities)
+ *  k_scale, v_scale : [num_blocks, Hkv] float, fp8 only (NULL for bf16).
+ *      The value of a stored code c in block p, head h is
+ *      decode(c) * scale[p, h] ([B] "FP8 KV cache": dequantise on read;
+ *      one scale per block and kv head).
+ *  block_tables : [B, max_blocks] int32.  Logical block j of sequence b
+ *      lives in physical block block_tables[b, j]; token t of sequence b
+ *      is slot t % block_size of logical block t / block_size
+ *      ([B] "PagedAttention": the block table maps logical blocks to
+ *      physical ones).  Several tables may name the same physical block
+ *      (shared prefixes, [B] "PagedAttention" / [A] prefix caching).
+ *  context_lens : [B] int32, the number of tokens of each sequence,
+ *      INCLUDING the token appended in the current decode step ([B] "What
+ *      the KV Cache Stores and Why": a step computes K, V for the new
+ *      token only and then attends the new query over every cached token).
+ *
+ * Table preconditions (not checked on the device)
+ * -----------------------------------------------
+ *  0 <= context_lens[b] <= max_blocks * block_size;
+ *  0 <= block_tables[b, j] < num_blocks for j < ceil(context_lens[b] / block_size);
+ *  entries past that are never read;
+ *  paged_kv_append must not target a block that another table also names.
+ *
+ * Cross-layer sharing ([A] "What is cross-layer KV sharing"): the layer ->
+ * group "shared-with" pointer is the caller passing the group's cache and
+ * scale pointers to the per-layer call; the kernels need nothing else.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_status {
+    PKV_OK = 0,
+    PKV_EINVAL = -1,        /* bad scalar, null or misaligned pointer      */
+    PKV_EUNSUPPORTED = -2,  /* shape outside the compiled kernel set       */
+    PKV_ELAUNCH = -3        /* the HIP runtime reported a launch failure   */
+};
+
+enum pkv_dtype {
+    PKV_BF16 = 0,
+    PKV_FP8_E4M3 = 1        /* OCP E4M3FN, per-(block, kv head) fp32 scale */
+};
+
+/* Supported shapes of this build: D in {64, 128}; block_size in {16, 32};
+ * 1 <= Hq / Hkv <= 16; Hq % Hkv == 0. */
+
+/*
+ * paged_kv_append -- write the decode step's new K and V rows into the cache.
+ *
+ * [B] "What the KV Cache Stores and Why": each generation step computes
+ * K and V for the new token only and stores them beside the cached ones.
+ * For each sequence b with T = context_lens[b] > 0 the new token is at
+ * logical position t = T - 1, so for every kv head h
+ *     k_cache[block_tables[b, t / block_size], t % block_size, h, :] = k_new[b, h, :]
+ * (likewise V).  Sequences with T == 0 are skipped.
+ *
+ * PKV_BF16: the bf16 bits are copied unchanged.
+ * PKV_FP8_E4M3 ([B] "FP8 KV cache": quantise on write with a scale):
+ *     code = E4M3FN_rne_satfinite( float(x) / scale[p, h] )
+ *     using the block's existing scale (binary32 division, correctly
+ *     rounded; ties to even; magnitudes beyond 448 saturate to +-448;
+ *     NaN -> 0x7F).
+ *
+ *  k_new, v_new : [B, Hkv, D] bf16 bits (device)
+ *  k_cache, v_cache, k_scale, v_scale, block_tables, context_lens : as above
+ *  Every byte other than the B x Hkv new rows is left unchanged.
+ *  Alignment: k_new/v_new/caches 16 bytes (8 for fp8 caches).
+ */
+int paged_kv_append(const uint16_t* k_new, const uint16_t* v_new,
+                    void* k_cache, void* v_cache,
+                    const float* k_scale, const float* v_scale,
+                    const int32_t* block_tables, int32_t max_blocks,
+                    const int32_t* context_lens,
+                    int32_t B, int32_t Hkv, int32_t D, int32_t block_size,
+                    int32_t num_blocks, int32_t kv_dtype, void* stream);
+
+/*
+ * paged_decode_attention -- one query token per sequence attends over all of
+ * its cached K/V, gathered through the block table.
+ *
+ * [B] "What the KV Cache Stores and Why" (attend the new Q over every
+ * cached K, V), [B] "PagedAttention" (the kernel locates each token's block
+ * through the table), [B] "Attention Variants" (grouped-query heads: query
+ * head hq reads kv head hq / (Hq / Hkv)).  The attention itself is
+ * standard softmax attention with an explicit scale (the pages do not
+ * spell it out):
+ *     s_t   = scale * dot(query[b, hq, :], K_t)            t in [0, T_b)
+ *     out   = sum_t softmax(s)_t * V_t
+ *     lse   = ln sum_t exp(s_t)
+ * computed in fp32 from bf16 (or dequantised fp8) inputs.
+ *
+ *  query : [B, Hq, D] bf16 bits
+ *  scale : softmax scale, usually 1/sqrt(D)
+ *
+ * split_tokens == 0 (single pass): writes out [B, Hq, D] float and, when
+ *     lse_out is non-NULL, lse_out [B, Hq] float.  partial_out, partial_lse
+ *     and max_splits are ignored.  A sequence with T == 0 gets out = 0,
+ *     lse = -inf.
+ * split_tokens > 0 (split context, a multiple of block_size): the context
+ *     of sequence b is cut into ceil(T_b / split_tokens) consecutive
+ *     ranges [s*S, min(T_b, (s+1)*S)), each attended independently (long
+ *     contexts are a bandwidth problem, [B] "Two Costs: Capacity and
+ *     Bandwidth"; independent ranges keep every compute unit streaming).
+ *     Writes the normalised partial outputs and their natural-log lse:
+ *         partial_out [B, Hq, max_splits, D] float
+ *         partial_lse [B, Hq, max_splits]    float
+ *     for s < ceil(T_b / S); other entries are untouched.  out and lse_out
+ *     are NOT written: combine the partials with split_context_reduce on
+ *     the same stream.  Requires max_splits >= ceil(max_b T_b / S).
+ *
+ *  Alignment: query, caches, out and partial_out 16 bytes.
+ */
+int paged_decode_attention(const uint16_t* query,
+                           const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t block_size, int32_t num_blocks,
+                           int32_t kv_dtype, float scale,
+                           int32_t split_tokens,
+                           float* out,
+                           float* partial_out, float* partial_lse,
+                           int32_t max_splits, float* lse_out, void* stream);
+
+/*
+ * split_context_reduce -- combine split-context partials into the final
+ * output with the log-sum-exp identity (not on the pages; it is the exact
+ * rule for softmax attention over disjoint key sets):
+ *     M   = max_s lse_s,   w_s = exp(lse_s - M)
+ *     out = sum_s w_s * o_s / sum_s w_s,   lse = M + ln sum_s w_s
+ * over the ceil(T_b / split_tokens) live splits of each sequence.  A split
+ * with lse_s = -inf (no tokens) carries no weight; if every split is
+ * -inf the result is out = 0, lse = -inf.
+ *
+ *  partial_out [B, Hq, max_splits, D], partial_lse [B, Hq, max_splits] float
+ *  out [B, Hq, D] float; lse_out [B, Hq] float or NULL.
+ *  Alignment: partial_out and out 16 bytes.
+ */
+int split_context_reduce(const float* partial_out, const float* partial_lse,
+                         const int32_t* context_lens,
+                         int32_t B, int32_t Hq, int32_t D,
+                         int32_t split_tokens, int32_t max_splits,
+                         float* out, float* lse_out, void* stream);
+
+/* Human-readable name of a pkv_status value (static storage). */
+const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,170 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of libpagedkv.so (C ABI in include/pagedkv.h).  Every
+step of the computation runs in the HIP kernels of that library; this
+module only turns torch tensors into pointers and sizes.  PyTorch provides
+device memory and streams, nothing else.  If the library is missing the
+import fails: there is no fallback.
+
+Entry points (same names as the C ABI):
+    paged_kv_append(...)          write the step's new K/V rows into the cache
+    paged_decode_attention(...)   attention of one query per sequence over
+                                  its block-table-gathered cache
+    split_context_reduce(...)     log-sum-exp merge of split-context partials
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, -1, -2, -3
+PKV_BF16, PKV_FP8_E4M3 = 0, 1
+
+EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
+           "pkv_status_string")
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run __graft_entry__.build() "
+            "(or python paged_kv_cache_273_amd/_build.py) first")
+    L = C.CDLL(LIB_PATH)
+    P, I = C.c_void_p, C.c_int32
+    L.paged_kv_append.restype = C.c_int
+    L.paged_kv_append.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P]
+    L.paged_decode_attention.restype = C.c_int
+    L.paged_decode_attention.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, C.c_float,
+                                         I, P, P, P, I, P, P]
+    L.split_context_reduce.restype = C.c_int
+    L.split_context_reduce.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
+    L.pkv_status_string.restype = C.c_char_p
+    L.pkv_status_string.argtypes = [C.c_int]
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PagedKVError(fn, status, _lib.pkv_status_string(status).decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+_BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _kv_dtype(cache: torch.Tensor) -> int:
+    if cache.dtype in _BF16_BITS:
+        return PKV_BF16
+    if cache.dtype in _FP8_CODES:
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported cache dtype {cache.dtype}")
+
+
+def _need(t: torch.Tensor, dtypes, name: str):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
+                    k_scale=None, v_scale=None, stream=None) -> None:
+    """k_new/v_new [B, Hkv, D] bf16; caches [num_blocks, block_size, Hkv, D]
+    (bf16 bits or E4M3FN codes); block_tables [B, max_blocks] int32;
+    context_lens [B] int32 (including the new token)."""
+    _need(k_new, _BF16_BITS, "k_new")
+    _need(v_new, _BF16_BITS, "v_new")
+    _need(block_tables, (torch.int32,), "block_tables")
+    _need(context_lens, (torch.int32,), "context_lens")
+    B, Hkv, D = k_new.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    st = _lib.paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                              block_tables.shape[1], _ptr(context_lens), B, Hkv, D, bs, nb,
+                              _kv_dtype(k_cache), _stream(stream))
+    _check("paged_kv_append", st)
+
+
+def paged_decode_attention(query, k_cache, v_cache, block_tables, context_lens, scale, *,
+                           out=None, lse_out=None, split_tokens=0, partial_out=None,
+                           partial_lse=None, k_scale=None, v_scale=None, stream=None):
+    """query [B, Hq, D] bf16.  split_tokens == 0: writes out [B, Hq, D] float32
+    (and lse_out [B, Hq]) and returns out.  split_tokens > 0: writes
+    partial_out [B, Hq, max_splits, D] / partial_lse [B, Hq, max_splits] and
+    returns them (combine with split_context_reduce)."""
+    _need(query, _BF16_BITS, "query")
+    _need(block_tables, (torch.int32,), "block_tables")
+    _need(context_lens, (torch.int32,), "context_lens")
+    B, Hq, D = query.shape
+    nb, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    max_splits = 0
+    if split_tokens == 0:
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+        _need(out, (torch.float32,), "out")
+    else:
+        if partial_out is None or partial_lse is None:
+            raise ValueError("split mode needs partial_out and partial_lse")
+        _need(partial_out, (torch.float32,), "partial_out")
+        _need(partial_lse, (torch.float32,), "partial_lse")
+        max_splits = partial_out.shape[2]
+    st = _lib.paged_decode_attention(
+        _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, nb,
+        _kv_dtype(k_cache), float(scale), int(split_tokens), _ptr(out), _ptr(partial_out),
+        _ptr(partial_lse), max_splits, _ptr(lse_out), _stream(stream))
+    _check("paged_decode_attention", st)
+    return out if split_tokens == 0 else (partial_out, partial_lse)
+
+
+def split_context_reduce(partial_out, partial_lse, context_lens, split_tokens, *, out=None,
+                         lse_out=None, stream=None):
+    """Merges partials [B, Hq, max_splits, D] into out [B, Hq, D] float32."""
+    _need(partial_out, (torch.float32,), "partial_out")
+    _need(partial_lse, (torch.float32,), "partial_lse")
+    B, Hq, ms, D = partial_out.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=partial_out.device)
+    st = _lib.split_context_reduce(_ptr(partial_out), _ptr(partial_lse), _ptr(context_lens), B,
+                                   Hq, D, int(split_tokens), ms, _ptr(out), _ptr(lse_out),
+                                   _stream(stream))
+    _check("split_context_reduce", st)
+    return out
+
+
+def max_splits_for(max_context: int, split_tokens: int) -> int:
+    """Number of partial slots a sequence of max_context tokens needs."""
+    return max(1, (int(max_context) + split_tokens - 1) // split_tokens)

@@ -1,0 +1,176 @@
+// abi.hip -- the C ABI of libpagedkv.so (declared in include/pagedkv.h).
+// Host-side argument checks, then one launch on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "pkv_kernels.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n)
+{
+    return ((uintptr_t)p % n) == 0;
+}
+
+bool supported_d(int32_t D)
+{
+    return D == 64 || D == 128;
+}
+
+bool supported_bs(int32_t bs)
+{
+    return bs == 16 || bs == 32;
+}
+
+int launched(hipError_t e)
+{
+    return e == hipSuccess ? PKV_OK : PKV_ELAUNCH;
+}
+
+constexpr int32_t kMaxGroup = 16;     // query heads per kv head (one MFMA column tile)
+constexpr int32_t kMaxSplits = 16384; // reduce keeps one weight per split in LDS
+
+} // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status)
+{
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported shape";
+    case PKV_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int paged_kv_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache, void* v_cache,
+                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                    int32_t max_blocks, const int32_t* context_lens, int32_t B, int32_t Hkv,
+                    int32_t D, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                    void* stream)
+{
+    if (B < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks <= 0)
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size))
+        return PKV_EUNSUPPORTED;
+    if (B == 0)
+        return PKV_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !context_lens)
+        return PKV_EINVAL;
+    const uintptr_t cache_align = kv_dtype == PKV_FP8_E4M3 ? 8 : 16;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, cache_align)
+        || !aligned(v_cache, cache_align))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    pkv::AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks = max_blocks;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.block_size = block_size;
+    a.kv_dtype = kv_dtype;
+    return launched(pkv::launch_append(a, (hipStream_t)stream));
+}
+
+int paged_decode_attention(const uint16_t* query, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                           float scale, int32_t split_tokens, float* out, float* partial_out,
+                           float* partial_lse, int32_t max_splits, float* lse_out, void* stream)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0
+        || max_blocks <= 0 || split_tokens < 0)
+        return PKV_EINVAL;
+    if (Hq % Hkv != 0 || !isfinite(scale))
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
+        return PKV_EUNSUPPORTED;
+    if (split_tokens > 0 && (split_tokens % block_size != 0 || max_splits <= 0))
+        return PKV_EINVAL;
+    if (B == 0)
+        return PKV_OK;
+    if (!query || !k_cache || !v_cache || !block_tables || !context_lens)
+        return PKV_EINVAL;
+    if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    if (split_tokens == 0) {
+        if (!out || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+            return PKV_EINVAL;
+    } else {
+        if (!partial_out || !partial_lse || !aligned(partial_out, 16))
+            return PKV_EINVAL;
+    }
+    pkv::DecodeArgs a;
+    a.query = query;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse_out = lse_out;
+    a.partial_out = partial_out;
+    a.partial_lse = partial_lse;
+    a.max_blocks = max_blocks;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.split_tokens = split_tokens;
+    a.max_splits = split_tokens > 0 ? max_splits : 1;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launched(pkv::launch_decode(a, D, block_size, kv_dtype, (hipStream_t)stream));
+}
+
+int split_context_reduce(const float* partial_out, const float* partial_lse,
+                         const int32_t* context_lens, int32_t B, int32_t Hq, int32_t D,
+                         int32_t split_tokens, int32_t max_splits, float* out, float* lse_out,
+                         void* stream)
+{
+    if (B < 0 || Hq <= 0 || D <= 0 || split_tokens <= 0 || max_splits <= 0)
+        return PKV_EINVAL;
+    if (max_splits > kMaxSplits)
+        return PKV_EUNSUPPORTED;
+    if (B == 0)
+        return PKV_OK;
+    if (!partial_out || !partial_lse || !context_lens || !out)
+        return PKV_EINVAL;
+    if (!aligned(partial_out, 16) || !aligned(out, 16))
+        return PKV_EINVAL;
+    pkv::ReduceArgs a;
+    a.partial_out = partial_out;
+    a.partial_lse = partial_lse;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse_out = lse_out;
+    a.B = B;
+    a.Hq = Hq;
+    a.D = D;
+    a.split_tokens = split_tokens;
+    a.max_splits = max_splits;
+    return launched(pkv::launch_reduce(a, (hipStream_t)stream));
+}
+
+} // extern "C"

@@ -1,0 +1,143 @@
+// append_reduce.hip -- the two small kernels around paged decode attention:
+//   * paged_kv_append: scatter the step's new K/V rows into their slots;
+//   * split_context_reduce: log-sum-exp merge of split-context partials.
+//
+// Pages cited:
+//   [B] "KV Cache Engineering: PagedAttention, Continuous Batching,
+//        Attention Variants, and the Bandwidth Wall"
+#include "pkv_device.hpp"
+#include "pkv_kernels.hpp"
+
+namespace pkv {
+namespace {
+
+// ---------------------------------------------------------------- append
+// [B] "What the KV Cache Stores and Why": a decode step computes K and V for
+// the new token only; it is stored at logical position T - 1 of its
+// sequence, i.e. slot (T-1) % bs of the physical block the table names for
+// logical block (T-1) / bs ([B] "PagedAttention").
+// One thread moves 8 elements (16 bytes of bf16 input) of one (b, h) row.
+// fp8 ([B] "FP8 KV cache"): code = E4M3FN(float(x) / scale[p, h]) with a
+// correctly rounded binary32 division.
+template <int FP8>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
+{
+    const int per_row = a.D / 8;
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)a.B * a.Hkv * per_row;
+    if (gid >= total)
+        return;
+    const int c = (int)(gid % per_row);
+    const int h = (int)((gid / per_row) % a.Hkv);
+    const int b = (int)(gid / ((long long)per_row * a.Hkv));
+    const int T = a.context_lens[b];
+    if (T <= 0)
+        return;
+    const int t = T - 1;
+    const int p = a.block_tables[(size_t)b * a.max_blocks + t / a.block_size];
+    const int slot = t % a.block_size;
+    const size_t src = ((size_t)b * a.Hkv + h) * a.D + 8 * c;
+    const size_t dst = (((size_t)p * a.block_size + slot) * a.Hkv + h) * a.D + 8 * c;
+    const u32x4 kx = *(const u32x4*)(a.k_new + src);
+    const u32x4 vx = *(const u32x4*)(a.v_new + src);
+    if (!FP8) {
+        *(u32x4*)((uint16_t*)a.k_cache + dst) = kx;
+        *(u32x4*)((uint16_t*)a.v_cache + dst) = vx;
+        return;
+    }
+    const float ks = a.k_scale[(size_t)p * a.Hkv + h];
+    const float vs = a.v_scale[(size_t)p * a.Hkv + h];
+    u32x2 kq = {0u, 0u}, vq = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t kb = (kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t vb = (vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t kc = f32_to_e4m3_sat(bf16_bits_to_f32(kb) / ks);
+        const uint32_t vc = f32_to_e4m3_sat(bf16_bits_to_f32(vb) / vs);
+        kq[i / 4] |= kc << (8 * (i & 3));
+        vq[i / 4] |= vc << (8 * (i & 3));
+    }
+    *(u32x2*)((uint8_t*)a.k_cache + dst) = kq;
+    *(u32x2*)((uint8_t*)a.v_cache + dst) = vq;
+}
+
+// ---------------------------------------------------------------- reduce
+// One wave per (b, hq).  Lanes first take the live splits' lse values
+// (M = max, w_s = exp(lse_s - M), W = sum w_s), park w_s in LDS, then each
+// lane accumulates D/64 output elements over the splits.
+__global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a)
+{
+    extern __shared__ float w_lds[];
+    const int row = blockIdx.x;                 // b * Hq + hq
+    const int b = row / a.Hq;
+    const int lane = threadIdx.x;
+    const int T = a.context_lens[b];
+    const int ns = T > 0 ? (T + a.split_tokens - 1) / a.split_tokens : 0;
+    const float* pl = a.partial_lse + (size_t)row * a.max_splits;
+    const float* po = a.partial_out + (size_t)row * a.max_splits * a.D;
+    float* o = a.out + (size_t)row * a.D;
+
+    float m = -__builtin_inff();
+    for (int s = lane; s < ns; s += kWave)
+        m = fmaxf(m, pl[s]);
+    m = wave_max(m);
+    if (m == -__builtin_inff()) {
+        for (int d = lane; d < a.D; d += kWave)
+            o[d] = 0.f;
+        if (a.lse_out && lane == 0)
+            a.lse_out[row] = -__builtin_inff();
+        return;
+    }
+    float wsum = 0.f;
+    for (int s = lane; s < ns; s += kWave) {
+        const float l = pl[s];
+        const float w = (l == -__builtin_inff()) ? 0.f : __expf(l - m);
+        w_lds[s] = w;
+        wsum += w;
+    }
+    wsum = wave_sum(wsum);
+    __syncthreads();
+    const float inv = 1.0f / wsum;
+    for (int d = lane; d < a.D; d += kWave) {
+        float accv = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const float w = w_lds[s];
+            if (w != 0.f)
+                accv += w * po[(size_t)s * a.D + d];
+        }
+        o[d] = accv * inv;
+    }
+    if (a.lse_out && lane == 0)
+        a.lse_out[row] = m + __logf(wsum);
+}
+
+} // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream)
+{
+    const long long total = (long long)a.B * a.Hkv * (a.D / 8);
+    if (total <= 0)
+        return hipSuccess;
+    const long long blocks = (total + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL)
+        return hipErrorInvalidConfiguration;
+    if (a.kv_dtype == 1)
+        hipLaunchKernelGGL(append_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(append_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
+{
+    const long long rows = (long long)a.B * a.Hq;
+    if (rows <= 0)
+        return hipSuccess;
+    if (rows > 0x7FFFFFFFLL)
+        return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)a.max_splits * sizeof(float);
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kWave), lds, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace pkv

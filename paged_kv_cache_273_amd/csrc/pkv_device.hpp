@@ -1,0 +1,121 @@
+// pkv_device.hpp -- device-side helpers shared by the gfx950 kernels of
+// libpagedkv.so (bf16 / fp8 conversions, MFMA and cross-lane wrappers).
+//
+// Pages cited: [B] "KV Cache Engineering: PagedAttention, Continuous
+// Batching, Attention Variants, and the Bandwidth Wall".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16x16x32 bf16 matrix-core product, fp32 accumulate.  Operand layout on
+// a 64-lane wave (q = lane / 16, r = lane % 16):
+//   A (16 x 32): lane holds A[r][k] for its 8 k-slots of group q
+//   B (32 x 16): lane holds B[k][r] for the same 8 k-slots of group q
+//   C (16 x 16): lane holds C[4q + i][r], i = 0..3
+// The contraction pairs A's and B's element i of lane group q, so any
+// assignment of the 32 contraction indices to (q, i) slots works as long
+// as A and B use the same one.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Two OCP E4M3FN codes (bytes 2*HI, 2*HI+1 of w) -> two bf16, exact:
+// every E4M3FN value, subnormals included, is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// 16 fp8 codes (one 16-byte load) -> 16 bf16 (two 8-element operands).
+__device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 codes, u32x4& lo, u32x4& hi)
+{
+    lo[0] = fp8x2_to_bf16x2<false>(codes[0]);
+    lo[1] = fp8x2_to_bf16x2<true>(codes[0]);
+    lo[2] = fp8x2_to_bf16x2<false>(codes[1]);
+    lo[3] = fp8x2_to_bf16x2<true>(codes[1]);
+    hi[0] = fp8x2_to_bf16x2<false>(codes[2]);
+    hi[1] = fp8x2_to_bf16x2<true>(codes[2]);
+    hi[2] = fp8x2_to_bf16x2<false>(codes[3]);
+    hi[3] = fp8x2_to_bf16x2<true>(codes[3]);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+{
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Butterfly exchange across lanes (lane ^ mask) through ds_bpermute.
+__device__ __forceinline__ float xor_shuffle(float v, int mask)
+{
+    int lane = __lane_id();
+    int src = (lane ^ mask) << 2;
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fmaxf(v, xor_shuffle(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += xor_shuffle(v, m);
+    return v;
+}
+
+// binary32 -> OCP E4M3FN, round to nearest even, saturating to +-448,
+// NaN -> 0x7F.  Normal results keep the top 3 mantissa bits with an
+// integer round-half-even on the 20 dropped bits and rebias the exponent
+// (127 -> 7); results below 2^-6 are multiples of 2^-9, obtained as
+// rint(|y| * 512) (exact scaling, hardware round-half-even).
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float y)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, y);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return 0x7Fu;                           // NaN
+    if (a >= 0x43E00000u)
+        return sign | 0x7Eu;                    // |y| >= 448 (and inf)
+    if (a >= 0x3C800000u) {                     // |y| >= 2^-6: normal code
+        uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        return sign | (r - (120u << 3));
+    }
+    float m = __builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+    return sign | (uint32_t)m;                  // 0..8 (8 == smallest normal)
+}
+
+} // namespace pkv

@@ -1,0 +1,52 @@
+// pkv_kernels.hpp -- launch-side declarations shared by the kernel sources
+// and the C ABI shim of libpagedkv.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    void* k_cache;
+    void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t max_blocks, B, Hkv, D, block_size, kv_dtype;
+};
+
+struct DecodeArgs {
+    const uint16_t* query;
+    const void* k_cache;
+    const void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* out;           // single pass
+    float* lse_out;       // single pass, may be null
+    float* partial_out;   // split
+    float* partial_lse;   // split
+    int32_t max_blocks, B, Hq, Hkv, G, split_tokens, max_splits;
+    float scale_log2;     // softmax scale * log2(e)
+};
+
+struct ReduceArgs {
+    const float* partial_out;
+    const float* partial_lse;
+    const int32_t* context_lens;
+    float* out;
+    float* lse_out;
+    int32_t B, Hq, D, split_tokens, max_splits;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype,
+                         hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
+} // namespace pkv
