@@ -26,14 +26,6 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved KV-read GB/s (% of HBM peak) + decode tokens/s, paged decode attn 1 GPU"
 HBM_PEAK_GBS = 8000.0
 
-# split_tokens used for each workload (0 = single pass)
-DEFAULT_SPLIT = {
-    "llama70b_b64_ragged1k_16k_bs32": 1024,
-    "llama70b_b4_ctx32k_split512_prefix2k": 512,
-    "llama8b_b32_ctx4096_bs16": 0,
-    "tiny_b4_hq8_hkv2_d64_bs16": 0,
-    "fp8_36layers_groups4_b32_ctx2k_8k": 0,
-}
 DEFAULT_WORKLOAD = "llama70b_b64_ragged1k_16k_bs32"
 
 
@@ -43,7 +35,11 @@ def _args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--split", type=int, default=None, help="split_tokens (default per workload)")
+    p.add_argument("--mode", default="auto", choices=["auto", "balanced", "split", "single"],
+                   help="attention schedule: work-balanced, fixed splits + reduce, or one "
+                        "wave per (sequence, kv head); auto = the workload's own split size "
+                        "if it has one, else balanced")
+    p.add_argument("--split", type=int, default=None, help="split_tokens for --mode split")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -68,7 +64,12 @@ def main():
     from synthetic import generate, make_workload
 
     wl = make_workload(a.workload)
-    S = DEFAULT_SPLIT.get(wl.name, 0) if a.split is None else a.split
+    mode = a.mode
+    if mode == "auto":
+        mode = "split" if wl.split_tokens > 0 else "balanced"
+    S = 0
+    if mode == "split":
+        S = a.split if a.split is not None else (wl.split_tokens or 512)
     dev = torch.device("cuda:0")
     t_gen = time.time()
     groups = [0] if wl.kv_dtype == "bf16" else [0]
@@ -112,6 +113,7 @@ def main():
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     po = torch.empty((wl.B, wl.Hq, ms, wl.D), dtype=torch.float32, device=dev) if S else None
     pl = torch.empty((wl.B, wl.Hq, ms), dtype=torch.float32, device=dev) if S else None
+    ws = pkv.make_workspace(q, k) if mode == "balanced" else None
 
     ev = []  # (start, end) around each attention launch in the timed region
 
@@ -120,15 +122,18 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        if S:
+        if mode == "split":
             pkv.paged_decode_attention(q, k, v, bt, cl, scale, split_tokens=S, partial_out=po,
                                        partial_lse=pl, k_scale=ks, v_scale=vs)
+        elif mode == "balanced":
+            pkv.paged_decode_attention_balanced(q, k, v, bt, cl, scale, workspace=ws, out=out,
+                                                k_scale=ks, v_scale=vs)
         else:
             pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks, v_scale=vs)
         if record:
             e1.record()
             ev.append((e0, e1))
-        if S:
+        if mode == "split":
             pkv.split_context_reduce(po, pl, cl, S, out=out)
 
     if a.calibrate_copy:
@@ -154,8 +159,8 @@ def main():
     traffic = None
     try:
         tj = json.load(open(a.traffic_json))
-        rec = tj.get(wl.name)
-        if rec and rec.get("split_tokens") == S:
+        rec = tj.get(f"{wl.name}:{mode}")
+        if rec:
             traffic = rec.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -183,13 +188,18 @@ def main():
             "workload": wl.name, "batch": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
             "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
             "ctx_sum": int(ctx.sum()), "ctx_mean": round(float(ctx.mean()), 1),
-            "ctx_min": int(ctx.min()), "ctx_max": int(ctx.max()), "split_tokens": S,
-            "num_blocks": inp.num_blocks, "ideal_kv_bytes_per_step": ideal,
-            "step": "paged_kv_append + paged_decode_attention"
-                    + (" + split_context_reduce" if S else ""),
+            "ctx_min": int(ctx.min()), "ctx_max": int(ctx.max()), "schedule": mode,
+            "split_tokens": S, "num_blocks": inp.num_blocks, "ideal_kv_bytes_per_step": ideal,
+            "step": {"split": "paged_kv_append + paged_decode_attention(split) + "
+                              "split_context_reduce",
+                     "balanced": "paged_kv_append + paged_decode_attention_balanced "
+                                 "(decode + log-sum-exp merge of cut units)",
+                     "single": "paged_kv_append + paged_decode_attention"}[mode],
         },
         "roofline": {
-            "bound": "hbm", "kernel": "decode_kernel (paged_decode_attention)",
+            "bound": "hbm",
+            "kernel": {"split": "decode_kernel (split)", "single": "decode_kernel",
+                       "balanced": "decode_balanced_kernel + balanced_merge_kernel"}[mode],
             "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": ideal,

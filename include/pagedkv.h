@@ -19,8 +19,9 @@
  *  * Ownership: the caller owns and allocates everything (pools, scales,
  *    tables, lengths, partials, outputs).  The library allocates nothing,
  *    frees nothing, never synchronises and keeps no state between calls;
- *    each call only enqueues kernels on `stream` and returns.  Calls are
- *    thread-safe.
+ *    each call only enqueues kernels on `stream` and returns (the balanced
+ *    decode also reads the current device's compute-unit count).  Calls
+ *    are thread-safe.
  *  * Errors: scalar arguments and pointer alignment are checked on the
  *    host before anything is launched.  A bad argument returns
  *    PKV_EINVAL, a shape outside the compiled kernel set returns
@@ -184,6 +185,52 @@ int split_context_reduce(const float* partial_out, const float* partial_lse,
                          int32_t B, int32_t Hq, int32_t D,
                          int32_t split_tokens, int32_t max_splits,
                          float* out, float* lse_out, void* stream);
+
+/*
+ * paged_decode_attention_balanced -- the same operation as the single-pass
+ * mode of paged_decode_attention (same arguments, same out / lse_out),
+ * scheduled for ragged batches.
+ *
+ * Decode time is the bytes streamed ([B] "Two Costs: Capacity and
+ * Bandwidth"); with ragged context lengths ([B] "Continuous Batching":
+ * sequences of every length share one decode iteration) a fixed
+ * one-unit-per-(sequence, head) grid leaves most compute units idle
+ * while the longest sequences finish.  Here the 32-token tiles of all
+ * (sequence, kv head) pairs form one list that is cut into as many equal
+ * ranges as the GPU runs waves at once; a pair cut by range boundaries is
+ * finished by a log-sum-exp merge of its pieces (second launch, same
+ * stream).
+ *
+ *  workspace       : device scratch of at least workspace_bytes, 16-byte
+ *                    aligned, owned by the caller; its contents on entry are
+ *                    irrelevant and on return unspecified.  Calls that share
+ *                    one workspace must be ordered on one stream.
+ *  workspace_bytes : >= paged_decode_workspace_size(Hq, Hkv, D, block_size,
+ *                    kv_dtype) for the device current at the call.
+ *  out, lse_out    : as in single-pass paged_decode_attention (T == 0 gives
+ *                    out = 0, lse = -inf).
+ *  Returns PKV_EINVAL if the workspace is too small; PKV_EUNSUPPORTED if
+ *  max_blocks * block_size exceeds 2^25 tokens.
+ */
+int paged_decode_attention_balanced(const uint16_t* query,
+                                    const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* block_tables, int32_t max_blocks,
+                                    const int32_t* context_lens,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t block_size, int32_t num_blocks,
+                                    int32_t kv_dtype, float scale,
+                                    void* workspace, int64_t workspace_bytes,
+                                    float* out, float* lse_out, void* stream);
+
+/*
+ * Bytes of workspace paged_decode_attention_balanced needs for these
+ * head counts and cache format on the current device (it depends on the
+ * device's compute-unit count), or a negative pkv_status.  Independent of
+ * the batch and of the context lengths.
+ */
+int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t block_size, int32_t kv_dtype);
 
 /* Human-readable name of a pkv_status value (static storage). */
 const char* pkv_status_string(int status);

@@ -30,7 +30,9 @@ int launched(hipError_t e)
 }
 
 constexpr int32_t kMaxGroup = 16;     // query heads per kv head (one MFMA column tile)
-constexpr int32_t kMaxSplits = 16384; // reduce keeps one weight per split in LDS
+constexpr int32_t kMaxSplits = 15360; // reduce keeps one weight per split in LDS
+// per-sequence token bound of the balanced path (64-sequence tile sums stay in int32)
+constexpr int64_t kMaxTokens = (int64_t)1 << 25;
 
 } // namespace
 
@@ -144,6 +146,102 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     return launched(pkv::launch_decode(a, D, block_size, kv_dtype, (hipStream_t)stream));
 }
 
+// Waves of the balanced decode on the current device: exactly the number
+// that can be resident at once, so every wave starts immediately.
+static int balanced_waves(int32_t D, int32_t block_size, int32_t kv_dtype)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int per_cu = pkv::balanced_blocks_per_cu(D, block_size, kv_dtype);
+    return cus * per_cu * pkv::decode_waves_per_group();
+}
+
+static int64_t balanced_bytes(int nwaves, int32_t G, int32_t D)
+{
+    return (int64_t)2 * nwaves * G * (D + 1) * (int64_t)sizeof(float);
+}
+
+int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                    int32_t kv_dtype)
+{
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
+        return PKV_EUNSUPPORTED;
+    const int n = balanced_waves(D, block_size, kv_dtype);
+    if (n <= 0)
+        return PKV_ELAUNCH;
+    return balanced_bytes(n, Hq / Hkv, D);
+}
+
+int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
+                                    const void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_tables,
+                                    int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                    int32_t num_blocks, int32_t kv_dtype, float scale,
+                                    void* workspace, int64_t workspace_bytes, float* out,
+                                    float* lse_out, void* stream)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0
+        || max_blocks <= 0 || workspace_bytes < 0)
+        return PKV_EINVAL;
+    if (Hq % Hkv != 0 || !isfinite(scale))
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
+        return PKV_EUNSUPPORTED;
+    if ((int64_t)max_blocks * block_size > kMaxTokens)
+        return PKV_EUNSUPPORTED;
+    if (B == 0)
+        return PKV_OK;
+    if (!query || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
+        return PKV_EINVAL;
+    if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)
+        || !aligned(out, 16) || !aligned(workspace, 16))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    const int n = balanced_waves(D, block_size, kv_dtype);
+    if (n <= 0)
+        return PKV_ELAUNCH;
+    const int32_t G = Hq / Hkv;
+    if (workspace_bytes < balanced_bytes(n, G, D))
+        return PKV_EINVAL;
+    pkv::DecodeArgs a;
+    a.query = query;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse_out = lse_out;
+    a.partial_out = nullptr;
+    a.partial_lse = nullptr;
+    a.max_blocks = max_blocks;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.split_tokens = 0;
+    a.max_splits = 1;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    pkv::BalanceArgs ws;
+    ws.part_out = (float*)workspace;
+    ws.part_lse = ws.part_out + (size_t)2 * n * G * D;
+    ws.nwaves = n;
+    return launched(pkv::launch_decode_balanced(a, ws, D, block_size, kv_dtype,
+                                                (hipStream_t)stream));
+}
+
 int split_context_reduce(const float* partial_out, const float* partial_lse,
                          const int32_t* context_lens, int32_t B, int32_t Hq, int32_t D,
                          int32_t split_tokens, int32_t max_splits, float* out, float* lse_out,
@@ -151,7 +249,7 @@ int split_context_reduce(const float* partial_out, const float* partial_lse,
 {
     if (B < 0 || Hq <= 0 || D <= 0 || split_tokens <= 0 || max_splits <= 0)
         return PKV_EINVAL;
-    if (max_splits > kMaxSplits)
+    if (max_splits > kMaxSplits || D % 4 != 0 || D > 1024)
         return PKV_EUNSUPPORTED;
     if (B == 0)
         return PKV_OK;

@@ -62,15 +62,36 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 }
 
 // ---------------------------------------------------------------- reduce
-// One wave per (b, hq).  Lanes first take the live splits' lse values
-// (M = max, w_s = exp(lse_s - M), W = sum w_s), park w_s in LDS, then each
-// lane accumulates D/64 output elements over the splits.
-__global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a)
+// One 256-thread work-group per (b, hq).  Threads first take the live
+// splits' lse values (M = max, w_s = exp(lse_s - M), W = sum w_s) and park
+// w_s in LDS; then thread (group g, column c) sums w_s * o_s over the
+// splits s = g, g + NG, ... for four output elements, so a work-group keeps
+// NG independent 16-byte loads per column in flight; the NG partial sums
+// meet in LDS.
+constexpr int kReduceThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, float* scratch, bool is_max)
 {
-    extern __shared__ float w_lds[];
-    const int row = blockIdx.x;                 // b * Hq + hq
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();
+    if (lane == 0)
+        scratch[wave] = v;
+    __syncthreads();
+    float r = scratch[0];
+    for (int i = 1; i < kReduceThreads / kWave; ++i)
+        r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
+    return r;
+}
+
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a)
+{
+    extern __shared__ f32x4 red[];               // [kReduceThreads] then weights
+    float* w_lds = (float*)(red + kReduceThreads);
+    float* scratch = (float*)red;
+    const int row = blockIdx.x;                  // b * Hq + hq
     const int b = row / a.Hq;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
     const int T = a.context_lens[b];
     const int ns = T > 0 ? (T + a.split_tokens - 1) / a.split_tokens : 0;
     const float* pl = a.partial_lse + (size_t)row * a.max_splits;
@@ -78,36 +99,47 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a)
     float* o = a.out + (size_t)row * a.D;
 
     float m = -__builtin_inff();
-    for (int s = lane; s < ns; s += kWave)
+    for (int s = tid; s < ns; s += kReduceThreads)
         m = fmaxf(m, pl[s]);
-    m = wave_max(m);
+    m = block_reduce(m, scratch, true);
     if (m == -__builtin_inff()) {
-        for (int d = lane; d < a.D; d += kWave)
+        for (int d = tid; d < a.D; d += kReduceThreads)
             o[d] = 0.f;
-        if (a.lse_out && lane == 0)
+        if (a.lse_out && tid == 0)
             a.lse_out[row] = -__builtin_inff();
         return;
     }
     float wsum = 0.f;
-    for (int s = lane; s < ns; s += kWave) {
+    for (int s = tid; s < ns; s += kReduceThreads) {
         const float l = pl[s];
         const float w = (l == -__builtin_inff()) ? 0.f : __expf(l - m);
         w_lds[s] = w;
         wsum += w;
     }
-    wsum = wave_sum(wsum);
-    __syncthreads();
-    const float inv = 1.0f / wsum;
-    for (int d = lane; d < a.D; d += kWave) {
-        float accv = 0.f;
-        for (int s = 0; s < ns; ++s) {
+    wsum = block_reduce(wsum, scratch, false);   // also orders the w_lds writes
+    const int cols = a.D / 4;
+    const int ng = kReduceThreads / cols;
+    const int col = tid % cols;
+    const int grp = tid / cols;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (grp < ng) {
+        for (int s = grp; s < ns; s += ng) {
             const float w = w_lds[s];
             if (w != 0.f)
-                accv += w * po[(size_t)s * a.D + d];
+                acc += w * *(const f32x4*)(po + (size_t)s * a.D + 4 * col);
         }
-        o[d] = accv * inv;
     }
-    if (a.lse_out && lane == 0)
+    __syncthreads();
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < cols) {
+        f32x4 t = red[tid];
+        for (int g = 1; g < ng; ++g)
+            t += red[g * cols + tid];
+        const float inv = 1.0f / wsum;
+        *(f32x4*)(o + 4 * tid) = t * inv;
+    }
+    if (a.lse_out && tid == 0)
         a.lse_out[row] = m + __logf(wsum);
 }
 
@@ -135,8 +167,9 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
         return hipSuccess;
     if (rows > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)a.max_splits * sizeof(float);
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kWave), lds, stream, a);
+    const size_t lds = kReduceThreads * sizeof(f32x4) + (size_t)a.max_splits * sizeof(float);
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kReduceThreads), lds, stream,
+                       a);
     return hipGetLastError();
 }
 

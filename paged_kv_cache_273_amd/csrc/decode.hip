@@ -32,8 +32,9 @@
 //     transposing 16-bit gather (row pitch padded by 8 bytes so the four
 //     lane groups hit disjoint banks); P enters as a hi + lo pair of bf16
 //     terms so the probabilities keep ~16 significant bits.
-// The next tile's K/V loads are issued before the current tile is
-// processed, so every wave keeps ~16 KB in flight.
+// The next tile's K/V loads are issued while the current tile is being
+// processed (into the registers the current tile has just released), so
+// every wave keeps up to 16 KB in flight with a single register set.
 //
 // The last tile of a range is masked: tokens at or past the range end
 // have their score selected to -inf and their V row zeroed before it
@@ -50,8 +51,28 @@
 namespace pkv {
 namespace {
 
-constexpr int kWavesPerGroup = 4;
+#ifndef PKV_WAVES_PER_GROUP
+#define PKV_WAVES_PER_GROUP 4
+#endif
+constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
+#ifndef PKV_MIN_WAVES_PER_EU
+#define PKV_MIN_WAVES_PER_EU 2
+#endif
 constexpr int kTile = 32;
+
+// K/V loads carry the non-temporal hint: every cached byte is read once
+// per decode step, and as streaming requests the L2 neither stalls on tag
+// allocation nor runs out of DRAM request credits (rocprofv3: TCC tag and
+// DRAM-credit stalls fall ~60x and the 8B-shape decode runs ~1.9x faster
+// than with default-policy loads).
+__device__ __forceinline__ u32x4 load_stream(const unsigned char* p)
+{
+#ifdef PKV_TEMPORAL_LOADS
+    return *(const u32x4*)p;
+#else
+    return __builtin_nontemporal_load((const u32x4*)p);
+#endif
+}
 
 template <int D, int FP8>
 struct Cfg {
@@ -90,57 +111,37 @@ template <int D, int FP8>
 struct Tile {
     u32x4 k[2][Cfg<D, FP8>::K_LOADS];
     u32x4 v[Cfg<D, FP8>::V_LOADS];
+};
+
+struct TileAddr {
     int pA, pB;            // physical blocks of tokens 0..15 / 16..31
     float ksA, ksB, vsA, vsB;
 };
 
-template <int D, int BS, int FP8, bool SPLIT>
-__global__ __launch_bounds__(kWavesPerGroup * kWave, 2)
-void decode_kernel(DecodeArgs a)
+// Unnormalised result of attending one token range: fp32 accumulators in
+// the O^T layout (lane (q, r): O^T[16dt + 4q + i][r]), the running max in
+// the exp2 domain and this lane's share of the normaliser.
+template <int D>
+struct RangeAcc {
+    f32x4 acc[D / 16];
+    float m;
+    float l;
+};
+
+// One wave attends the G query heads of kv head h of sequence b over the
+// logical tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.
+template <int D, int BS, int FP8>
+__device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
+                                             int h, int t_begin, int t_end, RangeAcc<D>& r)
 {
     using C = Cfg<D, FP8>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
-
     const int lane = __lane_id();
     const int q4 = lane >> 4;
     const int r16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = blockIdx.x * kWavesPerGroup + wave;
-
     const int Hkv = a.Hkv;
-    const int h = unit % Hkv;
-    int rest = unit / Hkv;
-    int split = 0;
-    if (SPLIT) {
-        split = rest % a.max_splits;
-        rest /= a.max_splits;
-    }
-    const int b = rest;
-    if (b >= a.B)
-        return;
-    const int T = a.context_lens[b];
-    int t_begin = 0, t_end = T;
-    if (SPLIT) {
-        t_begin = split * a.split_tokens;
-        if (t_begin >= T)
-            return;
-        t_end = min(T, t_begin + a.split_tokens);
-    }
     const int G = a.G;
-    const int hq = h * G + r16;              // this lane's query head column
+    const int hq = h * G + r16;
     const bool live_col = r16 < G;
-
-    if (t_end <= t_begin) {                  // empty sequence, single pass
-        if (live_col) {
-            float* o = a.out + ((size_t)b * a.Hq + hq) * D;
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-                *(f32x4*)(o + 16 * dt + 4 * q4) = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (a.lse_out && q4 == 0)
-                a.lse_out[(size_t)b * a.Hq + hq] = -__builtin_inff();
-        }
-        return;
-    }
 
     // Q^T operand: column r16 = query head h*G + r16 (zero past G).
     bf16x8 qf[C::KSTEPS];
@@ -172,55 +173,74 @@ void decode_kernel(DecodeArgs a)
         return __builtin_amdgcn_readlane(tbl, jj - base);
     };
 
+    // Addresses: a uniform (scalar) physical-block base plus a per-lane
+    // 32-bit offset that is the same for every tile.
     const unsigned char* kc = (const unsigned char*)a.k_cache;
     const unsigned char* vc = (const unsigned char*)a.v_cache;
-    const size_t tok_stride = (size_t)Hkv * C::ROW_BYTES;
-    const size_t head_off = (size_t)h * C::ROW_BYTES;
+    const uint32_t tok_stride = (uint32_t)Hkv * C::ROW_BYTES;
+    const size_t blk_stride = (size_t)BS * tok_stride;
+    const uint32_t head_off = (uint32_t)h * C::ROW_BYTES;
+    uint32_t k_off[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+        k_off[tau] = (uint32_t)(BS == 16 ? r16 : 16 * tau + r16) * tok_stride + head_off
+                     + 16 * q4;
+    uint32_t v_off[C::V_LOADS];
+#pragma unroll
+    for (int k = 0; k < C::V_LOADS; ++k) {
+        const int r = k * C::V_RPI + lane / C::V_LPR;
+        v_off[k] = (uint32_t)(BS == 16 ? (r & 15) : r) * tok_stride + head_off
+                   + 16 * (lane % C::V_LPR);
+    }
 
-    auto load_tile = [&](int t0, Tile<D, FP8>& tl) {
+    // Physical blocks (and fp8 scales) of the tile starting at t0.
+    auto tile_addr = [&](int t0) {
+        TileAddr ta;
         if (BS == 16) {
-            tl.pA = phys(t0 / 16);
-            tl.pB = phys(t0 / 16 + 1);
+            ta.pA = phys(t0 / 16);
+            ta.pB = phys(t0 / 16 + 1);
         } else {
-            tl.pA = phys(t0 / 32);
-            tl.pB = tl.pA;
+            ta.pA = phys(t0 / 32);
+            ta.pB = ta.pA;
         }
         if (FP8) {
-            tl.ksA = a.k_scale[(size_t)tl.pA * Hkv + h];
-            tl.vsA = a.v_scale[(size_t)tl.pA * Hkv + h];
-            tl.ksB = a.k_scale[(size_t)tl.pB * Hkv + h];
-            tl.vsB = a.v_scale[(size_t)tl.pB * Hkv + h];
+            ta.ksA = a.k_scale[(size_t)ta.pA * Hkv + h];
+            ta.vsA = a.v_scale[(size_t)ta.pA * Hkv + h];
+            ta.ksB = a.k_scale[(size_t)ta.pB * Hkv + h];
+            ta.vsB = a.v_scale[(size_t)ta.pB * Hkv + h];
         }
+        return ta;
+    };
+    auto load_k = [&](const TileAddr& ta, Tile<D, FP8>& tl) {
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            const int p = tau ? tl.pB : tl.pA;
-            const int slot = BS == 16 ? r16 : 16 * tau + r16;
-            const unsigned char* src = kc + ((size_t)p * BS + slot) * tok_stride + head_off;
+            const unsigned char* blk = kc + (size_t)(tau ? ta.pB : ta.pA) * blk_stride;
 #pragma unroll
             for (int c = 0; c < C::K_LOADS; ++c)
-                tl.k[tau][c] = *(const u32x4*)(src + 16 * (q4 + 4 * c));
+                tl.k[tau][c] = load_stream(blk + k_off[tau] + 64 * c);
         }
+    };
+    auto load_v = [&](const TileAddr& ta, Tile<D, FP8>& tl) {
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
-            const int r = k * C::V_RPI + lane / C::V_LPR;
-            const int p = (BS == 16 && k * C::V_RPI >= 16) ? tl.pB : tl.pA;
-            const int slot = BS == 16 ? (r & 15) : r;
-            const unsigned char* src = vc + ((size_t)p * BS + slot) * tok_stride + head_off;
-            tl.v[k] = *(const u32x4*)(src + 16 * (lane % C::V_LPR));
+            const int p = (BS == 16 && k * C::V_RPI >= 16) ? ta.pB : ta.pA;
+            const unsigned char* blk = vc + (size_t)p * blk_stride;
+            tl.v[k] = load_stream(blk + v_off[k]);
         }
     };
 
-    unsigned char* lds = lds_all + wave * C::LDS_BYTES;
-    f32x4 acc[C::DT];
+    f32x4 (&acc)[C::DT] = r.acc;
+    float& m_run = r.m;
+    float& l_run = r.l;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
         acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -__builtin_inff();
-    float l_run = 0.f;
+    m_run = -__builtin_inff();
+    l_run = 0.f;
     const float sl2 = a.scale_log2;
 
-    auto compute_tile = [&](int t0, const Tile<D, FP8>& tl, bool masked) {
-        // V rows -> LDS as bf16 (zeroed past the range end)
+    // V rows -> LDS as bf16 (zeroed past the range end).
+    auto stage_v = [&](int t0, const Tile<D, FP8>& tl, bool masked) {
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
             const int r = k * C::V_RPI + lane / C::V_LPR;
@@ -242,9 +262,10 @@ void decode_kernel(DecodeArgs a)
                 dst[1] = u32x2{v[2], v[3]};
             }
         }
+    };
 
-        // scores S^T[token][head] for the two 16-token halves
-        f32x4 sacc[2];
+    // scores S^T[token][head] of the two 16-token halves
+    auto qk = [&](const Tile<D, FP8>& tl, f32x4 (&sacc)[2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -260,11 +281,14 @@ void decode_kernel(DecodeArgs a)
                 }
             }
         }
+    };
 
+    // online softmax update and O^T += V^T . P^T from the staged V rows
+    auto softmax_pv = [&](int t0, const TileAddr& ta, const f32x4 (&sacc)[2], bool masked) {
         float s[8];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            const float f = FP8 ? sl2 * (tau ? tl.ksB : tl.ksA) : sl2;
+            const float f = FP8 ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float x = sacc[tau][i] * f;
@@ -296,8 +320,8 @@ void decode_kernel(DecodeArgs a)
         if (FP8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] *= tl.vsA;
-                p[4 + i] *= tl.vsB;
+                p[i] *= ta.vsA;
+                p[4 + i] *= ta.vsB;
             }
         }
         // P as a two-term bf16 split, p = hi + lo (about 16 significant
@@ -312,7 +336,6 @@ void decode_kernel(DecodeArgs a)
         const bf16x8 pb = as_bf16x8(pw);
         const bf16x8 pb_lo = as_bf16x8(pr);
 
-        // O^T[d][head] += V^T . P^T, V^T gathered from LDS
         const unsigned short* l16 = (const unsigned short*)lds;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
@@ -328,39 +351,388 @@ void decode_kernel(DecodeArgs a)
         }
     };
 
+    // One register set per wave: a tile's V registers are refilled with
+    // the next tile as soon as they are staged in LDS, its K registers as
+    // soon as the scores are formed; the next tile's 16 KB then stream in
+    // while this tile's softmax and PV product run.
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-    Tile<D, FP8> cur;
-    load_tile(t_begin, cur);
+    Tile<D, FP8> tl;
+    TileAddr ta = tile_addr(t_begin);
+    load_k(ta, tl);
+    load_v(ta, tl);
     for (int it = 0; it < ntiles - 1; ++it) {
-        Tile<D, FP8> nxt;
-        load_tile(t_begin + kTile * (it + 1), nxt);
-        compute_tile(t_begin + kTile * it, cur, false);
-        cur = nxt;
+        const int t0 = t_begin + kTile * it;
+        const TileAddr tn = tile_addr(t0 + kTile);
+        stage_v(t0, tl, false);
+        load_v(tn, tl);
+        f32x4 sacc[2];
+        qk(tl, sacc);
+        load_k(tn, tl);
+        softmax_pv(t0, ta, sacc, false);
+        ta = tn;
     }
-    compute_tile(t_begin + kTile * (ntiles - 1), cur, true);
+    {
+        const int t0 = t_begin + kTile * (ntiles - 1);
+        stage_v(t0, tl, true);
+        f32x4 sacc[2];
+        qk(tl, sacc);
+        softmax_pv(t0, ta, sacc, true);
+    }
 
-    // normaliser: sum the four lane groups of each head column
-    float l = l_run;
+}
+
+// Sums the per-lane normalisers of each head column; returns 1/l and the
+// natural-log lse of the range.
+template <int D>
+__device__ __forceinline__ void finish_range(const RangeAcc<D>& r, float& inv, float& lse)
+{
+    float l = r.l;
     l += xor_shuffle(l, 16);
     l += xor_shuffle(l, 32);
-    const float inv = 1.0f / l;
-    const float lse = (m_run + __builtin_log2f(l)) * kLn2;
+    inv = 1.0f / l;
+    lse = (r.m + __builtin_log2f(l)) * kLn2;
+}
+
+// Writes this lane's normalised output values of its head column.
+template <int D>
+__device__ __forceinline__ void store_row(float* o, const RangeAcc<D>& r, float inv)
+{
+    const int q4 = __lane_id() >> 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        *(f32x4*)(o + 16 * dt + 4 * q4) = r.acc[dt] * inv;
+}
+
+template <int D>
+__device__ __forceinline__ void store_empty_row(float* o)
+{
+    const int q4 = __lane_id() >> 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        *(f32x4*)(o + 16 * dt + 4 * q4) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Fixed partition: one wave per (b, h) over the whole context, or per
+// (b, h, split) over [s * split_tokens, min(T, (s + 1) * split_tokens)).
+template <int D, int BS, int FP8, bool SPLIT>
+__global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
+void decode_kernel(DecodeArgs a)
+{
+    using C = Cfg<D, FP8>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
+
+    const int q4 = __lane_id() >> 4;
+    const int r16 = __lane_id() & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = blockIdx.x * kWavesPerGroup + wave;
+    const int h = unit % a.Hkv;
+    int rest = unit / a.Hkv;
+    int split = 0;
+    if (SPLIT) {
+        split = rest % a.max_splits;
+        rest /= a.max_splits;
+    }
+    const int b = rest;
+    if (b >= a.B)
+        return;
+    const int T = a.context_lens[b];
+    int t_begin = 0, t_end = T;
+    if (SPLIT) {
+        t_begin = split * a.split_tokens;
+        if (t_begin >= T)
+            return;
+        t_end = min(T, t_begin + a.split_tokens);
+    }
+    const int hq = h * a.G + r16;
+    const bool live_col = r16 < a.G;
+    if (t_end <= t_begin) {                  // empty sequence, single pass
+        if (live_col) {
+            store_empty_row<D>(a.out + ((size_t)b * a.Hq + hq) * D);
+            if (a.lse_out && q4 == 0)
+                a.lse_out[(size_t)b * a.Hq + hq] = -__builtin_inff();
+        }
+        return;
+    }
+    RangeAcc<D> r;
+    attend_range<D, BS, FP8>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin, t_end, r);
+    float inv, lse;
+    finish_range<D>(r, inv, lse);
     if (!live_col)
         return;
-    float* o;
     if (SPLIT) {
         const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
-        o = a.partial_out + row * D;
+        store_row<D>(a.partial_out + row * D, r, inv);
         if (q4 == 0)
             a.partial_lse[row] = lse;
     } else {
-        o = a.out + ((size_t)b * a.Hq + hq) * D;
+        store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r, inv);
         if (a.lse_out && q4 == 0)
             a.lse_out[(size_t)b * a.Hq + hq] = lse;
     }
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-        *(f32x4*)(o + 16 * dt + 4 * q4) = acc[dt] * inv;
+}
+
+// ---------------------------------------------------------------- balanced
+// Work-balanced partition.  The work of the whole call is the list of
+// 32-token tiles of every (sequence, kv head) unit, in (b, h, tile) order;
+// wave w of N takes tiles [w*W/N, (w+1)*W/N) of that list, so every wave
+// streams the same number of bytes whatever the mix of context lengths.
+// A unit that lies inside one wave's range is written straight to `out`;
+// a unit cut by range boundaries leaves one normalised partial per piece
+// in the workspace (slot 2w for a wave's first piece, 2w+1 for its last)
+// and balanced_merge_kernel combines them with the log-sum-exp rule.
+
+__device__ __forceinline__ int tiles_of(int T)
+{
+    return (T + kTile - 1) / kTile;
+}
+
+// sum over sequences [0, b_end) of tiles_of(T_b) (same value in every lane)
+__device__ __forceinline__ long long tiles_before(const int32_t* ctx, int b_end)
+{
+    long long s = 0;
+    for (int c = 0; c < b_end; c += kWave) {
+        const int b = c + __lane_id();
+        s += wave_sum_i(b < b_end ? tiles_of(ctx[b]) : 0);
+    }
+    return s;
+}
+
+// Sequence whose tiles contain linear tile x of the (b, h, tile) list;
+// returns b and the tile count of the sequences before it.
+__device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int Hkv, long long x,
+                                            int& b_out, long long& before_out)
+{
+    long long base = 0;
+    for (int c = 0; c < B; c += kWave) {
+        const int b = c + __lane_id();
+        const int n = b < B ? tiles_of(ctx[b]) : 0;
+        const int incl = wave_inclusive_scan(n);
+        const unsigned long long hit = __ballot((base + incl) * Hkv > x);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            const int excl = __builtin_amdgcn_readlane(incl - n, l);
+            b_out = c + l;
+            before_out = base + excl;
+            return;
+        }
+        base += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    b_out = B;
+    before_out = base;
+}
+
+__device__ __forceinline__ long long range_start(long long w, long long total, long long N)
+{
+    return w * total / N;
+}
+
+template <int D, int BS, int FP8>
+__global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
+void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
+{
+    using C = Cfg<D, FP8>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
+
+    const int q4 = __lane_id() >> 4;
+    const int r16 = __lane_id() & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long w = (long long)blockIdx.x * kWavesPerGroup + wave;
+    const long long N = ws.nwaves;
+    if (w >= N)
+        return;
+    const int Hkv = a.Hkv;
+    const int G = a.G;
+    const long long total = tiles_before(a.context_lens, a.B) * Hkv;
+    const long long r0 = range_start(w, total, N);
+    const long long r1 = range_start(w + 1, total, N);
+    if (r0 >= r1)
+        return;
+    int b;
+    long long before;
+    locate_tile(a.context_lens, a.B, Hkv, r0, b, before);
+    int T = a.context_lens[b];
+    int n = tiles_of(T);
+    int h = (int)((r0 - before * Hkv) / n);
+    unsigned char* lds = lds_all + wave * C::LDS_BYTES;
+    long long x = r0;
+    int piece = 0;
+    while (true) {
+        const long long ustart = before * Hkv + (long long)h * n;
+        const long long uend = ustart + n;
+        const long long pend = uend < r1 ? uend : r1;
+        const int t_begin = (int)(x - ustart) * kTile;
+        const int t_end = min(T, (int)(pend - ustart) * kTile);
+        RangeAcc<D> r;
+        attend_range<D, BS, FP8>(a, lds, b, h, t_begin, t_end, r);
+        float inv, lse;
+        finish_range<D>(r, inv, lse);
+        const int hq = h * G + r16;
+        if (r16 < G) {
+            if (x == ustart && pend == uend) {
+                store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r, inv);
+                if (a.lse_out && q4 == 0)
+                    a.lse_out[(size_t)b * a.Hq + hq] = lse;
+            } else {
+                const size_t slot = 2 * (size_t)w + (piece == 0 ? 0 : 1);
+                store_row<D>(ws.part_out + (slot * G + r16) * D, r, inv);
+                if (q4 == 0)
+                    ws.part_lse[slot * G + r16] = lse;
+            }
+        }
+        ++piece;
+        x = pend;
+        if (x >= r1)
+            break;
+        if (++h == Hkv) {               // next sequence with a non-empty context
+            h = 0;
+            before += n;
+            do {
+                ++b;
+                T = a.context_lens[b];
+                n = tiles_of(T);
+            } while (n == 0);
+        }
+    }
+}
+
+// One 256-thread work-group per (b, hq): merges the pieces of its unit
+// (b, hq / G) when several waves shared it, writes zeros / -inf for an
+// empty sequence, and leaves a unit one wave finished alone untouched.
+// Threads take the pieces' lse values (M = max, w = exp(lse - M) parked in
+// LDS), then thread (group, column) accumulates four output elements over
+// every ng-th piece so all pieces' loads are in flight together.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float group_reduce(float v, float* scratch, bool is_max)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();
+    if (lane == 0)
+        scratch[wave] = v;
+    __syncthreads();
+    float r = scratch[0];
+    for (int i = 1; i < kMergeThreads / kWave; ++i)
+        r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
+    return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads)
+void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
+{
+    extern __shared__ f32x4 red[];                  // [kMergeThreads] then piece weights
+    float* wts = (float*)(red + kMergeThreads);
+    float* scratch = (float*)red;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;                     // b * Hq + hq
+    const int b = row / a.Hq;
+    const int hq = row % a.Hq;
+    const int G = a.G;
+    const int h = hq / G;
+    const int g = hq % G;
+    const int n = tiles_of(a.context_lens[b]);
+    float* o = a.out + (size_t)row * D;
+    if (n == 0) {
+        for (int d = tid; d < D; d += kMergeThreads)
+            o[d] = 0.f;
+        if (a.lse_out && tid == 0)
+            a.lse_out[row] = -__builtin_inff();
+        return;
+    }
+    const long long N = ws.nwaves;
+    const long long total = tiles_before(a.context_lens, a.B) * a.Hkv;
+    const long long ustart = tiles_before(a.context_lens, b) * a.Hkv + (long long)h * n;
+    const long long ulast = ustart + n - 1;
+    auto wave_of = [&](long long x) {
+        long long w = x * N / total;
+        while (w + 1 < N && range_start(w + 1, total, N) <= x)
+            ++w;
+        while (w > 0 && range_start(w, total, N) > x)
+            --w;
+        return w;
+    };
+    const long long wf = wave_of(ustart);
+    const long long wl = wave_of(ulast);
+    if (wf == wl)
+        return;
+    // Waves between wf and wl with an empty range (fewer tiles than waves)
+    // hold no piece of this unit.
+    auto piece_slot = [&](long long w) -> long long {
+        const long long r0 = range_start(w, total, N);
+        if (range_start(w + 1, total, N) <= r0)
+            return -1;
+        return 2 * w + ((w == wf && r0 < ustart) ? 1 : 0);
+    };
+    const int np = (int)(wl - wf + 1);
+    float m = -__builtin_inff();
+    for (int i = tid; i < np; i += kMergeThreads) {
+        const long long slot = piece_slot(wf + i);
+        if (slot >= 0)
+            m = fmaxf(m, ws.part_lse[slot * G + g]);
+    }
+    m = group_reduce(m, scratch, true);
+    float wsum = 0.f;
+    for (int i = tid; i < np; i += kMergeThreads) {
+        const long long slot = piece_slot(wf + i);
+        const float wt = slot >= 0 ? __expf(ws.part_lse[slot * G + g] - m) : 0.f;
+        wts[i] = wt;
+        wsum += wt;
+    }
+    wsum = group_reduce(wsum, scratch, false);      // also orders the wts writes
+    constexpr int cols = D / 4;
+    constexpr int ng = kMergeThreads / cols;
+    const int col = tid % cols;
+    const int grp = tid / cols;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = grp; i < np; i += ng) {
+        const float wt = wts[i];
+        if (wt != 0.f) {
+            const long long slot = piece_slot(wf + i);
+            acc += wt * *(const f32x4*)(ws.part_out + ((size_t)slot * G + g) * D + 4 * col);
+        }
+    }
+    __syncthreads();
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < cols) {
+        f32x4 t = red[tid];
+        for (int k = 1; k < ng; ++k)
+            t += red[k * cols + tid];
+        *(f32x4*)(o + 4 * tid) = t * (1.0f / wsum);
+    }
+    if (a.lse_out && tid == 0)
+        a.lse_out[row] = m + __logf(wsum);
+}
+
+template <int D, int BS, int FP8>
+int balanced_occupancy()
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8>),
+            kWavesPerGroup * kWave, 0) != hipSuccess)
+        return 0;
+    return blocks;
+}
+
+template <int D, int BS, int FP8>
+hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, hipStream_t stream)
+{
+    const long long groups = ((long long)ws.nwaves + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8>), dim3((unsigned)groups),
+                       dim3(kWavesPerGroup * kWave), 0, stream, a, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const long long rows = (long long)a.B * a.Hq;
+    if (rows > 0x7FFFFFFFLL)
+        return hipErrorInvalidConfiguration;
+    // a unit has at most nwaves + 1 pieces (one per wave plus an empty-range gap)
+    const size_t lds = kMergeThreads * sizeof(f32x4) + ((size_t)ws.nwaves + 1) * sizeof(float);
+    hipLaunchKernelGGL((balanced_merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads),
+                       lds, stream, a, ws);
+    return hipGetLastError();
 }
 
 template <int D, int BS, int FP8>
@@ -389,6 +761,39 @@ hipError_t launch_d_bs(const DecodeArgs& a, int kv_dtype, hipStream_t stream)
 }
 
 } // namespace
+
+int decode_waves_per_group()
+{
+    return kWavesPerGroup;
+}
+
+int balanced_blocks_per_cu(int D, int block_size, int kv_dtype)
+{
+#define PKV_OCC(d, bs)                                                                  \
+    if (D == d && block_size == bs)                                                    \
+        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1>() : balanced_occupancy<d, bs, 0>();
+    PKV_OCC(128, 16)
+    PKV_OCC(128, 32)
+    PKV_OCC(64, 16)
+    PKV_OCC(64, 32)
+#undef PKV_OCC
+    return 0;
+}
+
+hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
+                                  int block_size, int kv_dtype, hipStream_t stream)
+{
+#define PKV_BAL(d, bs)                                                                  \
+    if (D == d && block_size == bs)                                                    \
+        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1>(a, ws, stream)              \
+                             : launch_balanced_t<d, bs, 0>(a, ws, stream);
+    PKV_BAL(128, 16)
+    PKV_BAL(128, 32)
+    PKV_BAL(64, 16)
+    PKV_BAL(64, 32)
+#undef PKV_BAL
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype,
                          hipStream_t stream)

@@ -80,6 +80,37 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask)
                               __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
 }
 
+__device__ __forceinline__ int xor_shuffle_i(int v, int mask)
+{
+    int lane = __lane_id();
+    return __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, v);
+}
+
+// Value of lane (lane - delta), or 0 for the first `delta` lanes.
+__device__ __forceinline__ int shift_up_i(int v, int delta)
+{
+    int lane = __lane_id();
+    int r = __builtin_amdgcn_ds_bpermute((lane - delta) << 2, v);
+    return lane >= delta ? r : 0;
+}
+
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        v += shift_up_i(v, d);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += xor_shuffle_i(v, m);
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll

@@ -35,6 +35,14 @@ struct DecodeArgs {
     float scale_log2;     // softmax scale * log2(e)
 };
 
+// Workspace of the balanced decode: 2 partial slots per wave, each with
+// G rows of D floats and G lse values.
+struct BalanceArgs {
+    float* part_out;      // [2 * nwaves, G, D]
+    float* part_lse;      // [2 * nwaves, G]
+    int32_t nwaves;
+};
+
 struct ReduceArgs {
     const float* partial_out;
     const float* partial_lse;
@@ -48,5 +56,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype,
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
+                                  int block_size, int kv_dtype, hipStream_t stream);
+// resident work-groups per compute unit of the balanced kernel (0 on error)
+int balanced_blocks_per_cu(int D, int block_size, int kv_dtype);
+// waves per work-group of the decode kernels
+int decode_waves_per_group();
 
 } // namespace pkv

@@ -28,7 +28,8 @@ def pkv():
 def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["paged_kv_append", "paged_decode_attention",
-                            "split_context_reduce", "pkv_status_string"]), names
+                            "split_context_reduce", "paged_decode_attention_balanced",
+                            "paged_decode_workspace_size", "pkv_status_string"]), names
 
 
 def test_library_exports_every_declared_symbol(pkv):
@@ -90,8 +91,48 @@ def test_reduce_rejects(pkv):
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 0, 4, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 32, 0, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 32, 20000, f, None, None) == -2
+    assert L.split_context_reduce(f, f, f, 1, 8, 66, 32, 4, f, None, None) == -2
     assert L.split_context_reduce(f, f, None, 1, 8, 64, 32, 4, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 0, 8, 64, 32, 4, f, None, None) == 0
+
+
+def _balanced(pkv, **kw):
+    a = dict(B=1, Hq=8, Hkv=2, D=64, bs=16, nb=8, dt=0, scale=0.125, ws=0x1000, wsb=1 << 20,
+             out=0x1000, max_blocks=4)
+    a.update(kw)
+    f = 0x1000
+    return pkv.lib().paged_decode_attention_balanced(
+        f, f, f, None, None, f, a["max_blocks"], f, a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+        a["nb"], a["dt"], a["scale"], a["ws"], a["wsb"], a["out"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"Hq": 6, "Hkv": 4}, -1),
+    ({"D": 96}, -2),
+    ({"bs": 64}, -2),
+    ({"Hq": 64, "Hkv": 2}, -2),
+    ({"dt": 2}, -1),
+    ({"dt": 1}, -1),                     # fp8 without scales
+    ({"ws": None}, -1),                  # no workspace
+    ({"ws": 0x1004}, -1),                # misaligned workspace
+    ({"wsb": -5}, -1),
+    ({"max_blocks": 1 << 22}, -2),       # more than 2^25 tokens per sequence
+    ({"scale": float("inf")}, -1),
+])
+def test_balanced_rejects(pkv, kw, status):
+    assert _balanced(pkv, **kw) == status
+
+
+def test_balanced_empty_batch_is_a_no_op(pkv):
+    assert _balanced(pkv, B=0) == 0
+
+
+def test_workspace_size_rejects(pkv):
+    L = pkv.lib()
+    assert L.paged_decode_workspace_size(6, 4, 64, 16, 0) == -1
+    assert L.paged_decode_workspace_size(8, 2, 96, 16, 0) == -2
+    assert L.paged_decode_workspace_size(8, 2, 64, 8, 0) == -2
+    assert L.paged_decode_workspace_size(8, 2, 64, 16, 7) == -1
 
 
 def test_append_rejects(pkv):

@@ -233,3 +233,105 @@ def test_reduce_alone(orc, pkv):
     gl = lse.cpu().numpy()
     assert np.array_equal(np.isneginf(gl), np.isneginf(rlse))
     assert_close(np.where(np.isneginf(gl), 0, gl), rl, "reduce lse")
+
+
+# ---------------------------------------------------------------- balanced
+def run_balanced(pkv, d, layer=0, scale=None, append=True):
+    inp = d.inp
+    wl = inp.wl
+    sc = float(inp.scale) if scale is None else float(scale)
+    if append:
+        pkv.paged_kv_append(d.k_new, d.v_new, d.k, d.v, d.bt, d.cl, k_scale=d.ks,
+                            v_scale=d.vs)
+    ws = pkv.make_workspace(d.q[layer], d.k)
+    ws.fill_(0xFF)          # NaN garbage: the workspace contents on entry must not matter
+    lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device=dev())
+    out = pkv.paged_decode_attention_balanced(d.q[layer], d.k, d.v, d.bt, d.cl, sc,
+                                              workspace=ws, lse_out=lse, k_scale=d.ks,
+                                              v_scale=d.vs)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("scale", [None, 1.0])
+def test_balanced_tiny(orc, pkv, scale):
+    inp = generate(make_workload(TINY))
+    d = DeviceInputs(inp)
+    out, lse = run_balanced(pkv, d, scale=scale)
+    kp, vp = host_appended(orc, inp)
+    ref, rlse = _oracle(orc, inp, kp, vp, scale=scale)
+    assert_close(out, ref, "balanced out")
+    assert_close(lse, rlse, "balanced lse")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("G", [1, 8, 16])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_balanced_shapes(orc, pkv, D, bs, G, kv):
+    """Few tiles against thousands of waves: nearly every unit is cut into
+    one-tile pieces on different waves, so the merge carries the result."""
+    Hkv = 2
+    wl = make_workload(TINY, B=len(EDGE_CTX), Hq=G * Hkv, Hkv=Hkv, D=D, block_size=bs,
+                       ctx_fixed=EDGE_CTX, max_blocks=(300 + bs - 1) // bs + 1,
+                       pool="holes10", kv_dtype=kv, seed=2000 + D + bs + G)
+    inp = generate(wl)
+    print(f"balanced shape D={D} bs={bs} G={G} kv={kv}", flush=True)
+    if kv == "fp8":
+        kc, vc, ks, vs = fp8_group(orc, inp)
+        d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
+        kp, vp = host_appended(orc, inp, kv_dtype="fp8", k_pool=kc, v_pool=vc, ks=ks, vs=vs)
+        ref, rlse = _oracle(orc, inp, kp, vp, kv_dtype="fp8", ks=ks, vs=vs)
+    else:
+        d = DeviceInputs(inp)
+        kp, vp = host_appended(orc, inp)
+        ref, rlse = _oracle(orc, inp, kp, vp)
+    out, lse = run_balanced(pkv, d)
+    assert_close(out, ref, "balanced")
+    assert_close(lse, rlse, "balanced lse")
+
+
+def test_balanced_empty_and_ragged(orc, pkv):
+    ctx = (0, 5000, 0, 1, 33, 7000, 0, 64)
+    wl = make_workload("llama70b_b64_ragged1k_16k_bs32", B=len(ctx), ctx_fixed=ctx,
+                       max_blocks=220, Hq=16, Hkv=2)
+    inp = generate(wl)
+    d = DeviceInputs(inp)
+    out, lse = run_balanced(pkv, d)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for b in (0, 2, 6):
+        assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+    kp, vp = host_appended(orc, inp)
+    keep = [1, 3, 4, 5, 7]
+    sub = inp.context_lens.copy()
+    ref, rlse = _oracle(orc, inp, kp, vp)
+    assert_close(o[keep], ref[keep], "balanced ragged")
+    assert_close(l[keep], rlse[keep], "balanced ragged lse")
+    del sub
+
+
+def test_balanced_deterministic_and_placement_free(orc, pkv):
+    inp = generate(make_workload("llama70b_b64_ragged1k_16k_bs32", B=6, ctx_uniform=(1, 3000),
+                                 max_blocks=94))
+    kp, vp = host_appended(orc, inp)
+    d = DeviceInputs(inp, k_pool=kp, v_pool=vp)
+    a, la = run_balanced(pkv, d, append=False)
+    b, lb = run_balanced(pkv, d, append=False)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    kq, vq, tq = _permuted(inp, kp, vp, 7)
+    d2 = DeviceInputs(inp, k_pool=kq, v_pool=vq)
+    d2.bt = to_dev(tq)
+    c, lc = run_balanced(pkv, d2, append=False)
+    assert torch.equal(a, c) and torch.equal(la, lc)
+    ref, _ = _oracle(orc, inp, kp, vp)
+    assert_close(a, ref, "balanced")
+
+
+def test_balanced_workspace_too_small(pkv):
+    inp = generate(make_workload(TINY))
+    d = DeviceInputs(inp)
+    need = pkv.make_workspace(d.q[0], d.k).numel()
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=dev())
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_decode_attention_balanced(d.q[0], d.k, d.v, d.bt, d.cl, float(inp.scale),
+                                            workspace=ws)
