@@ -156,14 +156,7 @@ def main():
     step_s = wall / a.steps
     gbs = ideal / step_s / 1e9
     kern_gbs = ideal / kern_s / 1e9
-    traffic = None
-    try:
-        tj = json.load(open(a.traffic_json))
-        rec = tj.get(f"{wl.name}:{mode}")
-        if rec:
-            traffic = rec.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    traffic = _measured_traffic(a.traffic_json, f"{wl.name}:{mode}")
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -207,6 +200,25 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def _measured_traffic(path, key):
+    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes recorded in profiles/traffic.json, or None when there
+    is no record or the decode source has changed since it was taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(path)).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "paged_kv_cache_273_amd", "csrc", "decode.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("decode_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def _cpu_baseline(inp, wl, target_s):

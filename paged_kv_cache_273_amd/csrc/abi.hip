@@ -146,22 +146,23 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     return launched(pkv::launch_decode(a, D, block_size, kv_dtype, (hipStream_t)stream));
 }
 
-// Waves of the balanced decode on the current device: exactly the number
-// that can be resident at once, so every wave starts immediately.
-static int balanced_waves(int32_t D, int32_t block_size, int32_t kv_dtype)
+// Work-groups of the balanced decode on the current device: exactly the
+// number that can be resident at once, so every group starts immediately.
+static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype)
 {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    const int per_cu = pkv::balanced_blocks_per_cu(D, block_size, kv_dtype);
-    return cus * per_cu * pkv::decode_waves_per_group();
+    const int hg = pkv::balanced_head_group(Hkv);
+    return cus * pkv::balanced_groups_per_cu(D, block_size, kv_dtype, hg);
 }
 
-static int64_t balanced_bytes(int nwaves, int32_t G, int32_t D)
+static int64_t balanced_bytes(int ngroups, int32_t Hkv, int32_t G, int32_t D)
 {
-    return (int64_t)2 * nwaves * G * (D + 1) * (int64_t)sizeof(float);
+    const int64_t rows = (int64_t)2 * ngroups * pkv::balanced_head_group(Hkv) * G;
+    return rows * (D + 1) * (int64_t)sizeof(float);
 }
 
 int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
@@ -173,10 +174,10 @@ int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t 
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
         return PKV_EUNSUPPORTED;
-    const int n = balanced_waves(D, block_size, kv_dtype);
+    const int n = balanced_groups(Hkv, D, block_size, kv_dtype);
     if (n <= 0)
         return PKV_ELAUNCH;
-    return balanced_bytes(n, Hq / Hkv, D);
+    return balanced_bytes(n, Hkv, Hq / Hkv, D);
 }
 
 int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
@@ -208,11 +209,11 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
         return PKV_EINVAL;
     if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
         return PKV_EINVAL;
-    const int n = balanced_waves(D, block_size, kv_dtype);
+    const int n = balanced_groups(Hkv, D, block_size, kv_dtype);
     if (n <= 0)
         return PKV_ELAUNCH;
     const int32_t G = Hq / Hkv;
-    if (workspace_bytes < balanced_bytes(n, G, D))
+    if (workspace_bytes < balanced_bytes(n, Hkv, G, D))
         return PKV_EINVAL;
     pkv::DecodeArgs a;
     a.query = query;
@@ -235,9 +236,10 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     a.max_splits = 1;
     a.scale_log2 = scale * 1.4426950408889634f;
     pkv::BalanceArgs ws;
+    ws.head_group = pkv::balanced_head_group(Hkv);
+    ws.ngroups_launched = n;
     ws.part_out = (float*)workspace;
-    ws.part_lse = ws.part_out + (size_t)2 * n * G * D;
-    ws.nwaves = n;
+    ws.part_lse = ws.part_out + (size_t)2 * n * ws.head_group * G * D;
     return launched(pkv::launch_decode_balanced(a, ws, D, block_size, kv_dtype,
                                                 (hipStream_t)stream));
 }

@@ -472,14 +472,21 @@ void decode_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------- balanced
-// Work-balanced partition.  The work of the whole call is the list of
-// 32-token tiles of every (sequence, kv head) unit, in (b, h, tile) order;
-// wave w of N takes tiles [w*W/N, (w+1)*W/N) of that list, so every wave
-// streams the same number of bytes whatever the mix of context lengths.
-// A unit that lies inside one wave's range is written straight to `out`;
-// a unit cut by range boundaries leaves one normalised partial per piece
-// in the workspace (slot 2w for a wave's first piece, 2w+1 for its last)
-// and balanced_merge_kernel combines them with the log-sum-exp rule.
+// Work-balanced partition.  A work-group is a head group: HG waves, one per
+// kv head h = hg * HG + i, that walk the same token ranges together, so the
+// Hkv rows of every slot of a physical block are streamed at the same time
+// (rocprofv3 / timing: spreading the heads of a block over time costs
+// 12-16% of bandwidth).  The work of the call is the list of 32-token
+// tiles of every (sequence, head group) unit in (b, hg, tile) order;
+// work-group r of R takes tiles [r*W/R, (r+1)*W/R), R being the number of
+// work-groups the GPU holds at once, so every group streams the same bytes
+// whatever the mix of context lengths.  A unit inside one group's range is
+// written straight to `out`; a unit cut by range boundaries leaves one
+// normalised partial per piece in the workspace (slot 2r for a group's
+// first piece, 2r+1 for its last) and balanced_merge_kernel combines them
+// with the log-sum-exp rule.
+
+constexpr int kMaxHeadGroup = 8;
 
 __device__ __forceinline__ int tiles_of(int T)
 {
@@ -497,9 +504,10 @@ __device__ __forceinline__ long long tiles_before(const int32_t* ctx, int b_end)
     return s;
 }
 
-// Sequence whose tiles contain linear tile x of the (b, h, tile) list;
-// returns b and the tile count of the sequences before it.
-__device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int Hkv, long long x,
+// Sequence whose units contain linear tile x of the (b, hg, tile) list
+// (ngroups head groups per sequence); returns b and the tile count of the
+// sequences before it.
+__device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int ngroups, long long x,
                                             int& b_out, long long& before_out)
 {
     long long base = 0;
@@ -507,7 +515,7 @@ __device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int Hkv, 
         const int b = c + __lane_id();
         const int n = b < B ? tiles_of(ctx[b]) : 0;
         const int incl = wave_inclusive_scan(n);
-        const unsigned long long hit = __ballot((base + incl) * Hkv > x);
+        const unsigned long long hit = __ballot((base + incl) * ngroups > x);
         if (hit) {
             const int l = __builtin_ctzll(hit);
             const int excl = __builtin_amdgcn_readlane(incl - n, l);
@@ -521,70 +529,72 @@ __device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int Hkv, 
     before_out = base;
 }
 
-__device__ __forceinline__ long long range_start(long long w, long long total, long long N)
+__device__ __forceinline__ long long range_start(long long r, long long total, long long R)
 {
-    return w * total / N;
+    return r * total / R;
 }
 
 template <int D, int BS, int FP8>
-__global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
+__global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 {
     using C = Cfg<D, FP8>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_all[];  // HG slices
 
     const int q4 = __lane_id() >> 4;
     const int r16 = __lane_id() & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long w = (long long)blockIdx.x * kWavesPerGroup + wave;
-    const long long N = ws.nwaves;
-    if (w >= N)
-        return;
-    const int Hkv = a.Hkv;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head within group
+    const long long r = blockIdx.x;
+    const long long R = ws.ngroups_launched;
+    const int HG = ws.head_group;
+    const int ngroups = a.Hkv / HG;
     const int G = a.G;
-    const long long total = tiles_before(a.context_lens, a.B) * Hkv;
-    const long long r0 = range_start(w, total, N);
-    const long long r1 = range_start(w + 1, total, N);
+    const long long total = tiles_before(a.context_lens, a.B) * ngroups;
+    const long long r0 = range_start(r, total, R);
+    const long long r1 = range_start(r + 1, total, R);
     if (r0 >= r1)
         return;
     int b;
     long long before;
-    locate_tile(a.context_lens, a.B, Hkv, r0, b, before);
+    locate_tile(a.context_lens, a.B, ngroups, r0, b, before);
     int T = a.context_lens[b];
     int n = tiles_of(T);
-    int h = (int)((r0 - before * Hkv) / n);
+    int hg = (int)((r0 - before * ngroups) / n);
     unsigned char* lds = lds_all + wave * C::LDS_BYTES;
+    const int rows_per_slot = HG * G;
     long long x = r0;
     int piece = 0;
     while (true) {
-        const long long ustart = before * Hkv + (long long)h * n;
+        const long long ustart = before * ngroups + (long long)hg * n;
         const long long uend = ustart + n;
         const long long pend = uend < r1 ? uend : r1;
         const int t_begin = (int)(x - ustart) * kTile;
         const int t_end = min(T, (int)(pend - ustart) * kTile);
-        RangeAcc<D> r;
-        attend_range<D, BS, FP8>(a, lds, b, h, t_begin, t_end, r);
+        const int h = hg * HG + wave;
+        RangeAcc<D> acc;
+        attend_range<D, BS, FP8>(a, lds, b, h, t_begin, t_end, acc);
         float inv, lse;
-        finish_range<D>(r, inv, lse);
-        const int hq = h * G + r16;
+        finish_range<D>(acc, inv, lse);
         if (r16 < G) {
+            const int hq = h * G + r16;
             if (x == ustart && pend == uend) {
-                store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r, inv);
+                store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, acc, inv);
                 if (a.lse_out && q4 == 0)
                     a.lse_out[(size_t)b * a.Hq + hq] = lse;
             } else {
-                const size_t slot = 2 * (size_t)w + (piece == 0 ? 0 : 1);
-                store_row<D>(ws.part_out + (slot * G + r16) * D, r, inv);
+                const size_t slot = 2 * (size_t)r + (piece == 0 ? 0 : 1);
+                const size_t row = slot * rows_per_slot + wave * G + r16;
+                store_row<D>(ws.part_out + row * D, acc, inv);
                 if (q4 == 0)
-                    ws.part_lse[slot * G + r16] = lse;
+                    ws.part_lse[row] = lse;
             }
         }
         ++piece;
         x = pend;
         if (x >= r1)
             break;
-        if (++h == Hkv) {               // next sequence with a non-empty context
-            h = 0;
+        if (++hg == ngroups) {          // next sequence with a non-empty context
+            hg = 0;
             before += n;
             do {
                 ++b;
@@ -595,123 +605,115 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     }
 }
 
-// One 256-thread work-group per (b, hq): merges the pieces of its unit
-// (b, hq / G) when several waves shared it, writes zeros / -inf for an
-// empty sequence, and leaves a unit one wave finished alone untouched.
-// Threads take the pieces' lse values (M = max, w = exp(lse - M) parked in
-// LDS), then thread (group, column) accumulates four output elements over
-// every ng-th piece so all pieces' loads are in flight together.
-constexpr int kMergeThreads = 256;
-
-__device__ __forceinline__ float group_reduce(float v, float* scratch, bool is_max)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = is_max ? wave_max(v) : wave_sum(v);
-    __syncthreads();
-    if (lane == 0)
-        scratch[wave] = v;
-    __syncthreads();
-    float r = scratch[0];
-    for (int i = 1; i < kMergeThreads / kWave; ++i)
-        r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
-    return r;
-}
+// One wave per output row (b, hq): merges the pieces of its unit
+// (b, head group of hq) when several work-groups shared it, writes zeros /
+// -inf for an empty sequence, and leaves rows that one group finished
+// alone untouched.  Lane (p, c) owns four output elements (column c) and
+// every npg-th piece starting at p, so all pieces' loads are in flight
+// together; the npg partial sums meet through lane butterflies.
+constexpr int kMergeWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(kMergeThreads)
+__global__ __launch_bounds__(kMergeWaves * kWave)
 void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
 {
-    extern __shared__ f32x4 red[];                  // [kMergeThreads] then piece weights
-    float* wts = (float*)(red + kMergeThreads);
-    float* scratch = (float*)red;
-    const int tid = threadIdx.x;
-    const int row = blockIdx.x;                     // b * Hq + hq
-    const int b = row / a.Hq;
-    const int hq = row % a.Hq;
+    constexpr int cols = D / 4;
+    constexpr int npg = kWave / cols;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long row = (long long)blockIdx.x * kMergeWaves + wave;     // b * Hq + hq
+    if (row >= (long long)a.B * a.Hq)
+        return;
+    const int b = (int)(row / a.Hq);
+    const int hq = (int)(row % a.Hq);
     const int G = a.G;
+    const int HG = ws.head_group;
     const int h = hq / G;
-    const int g = hq % G;
+    const int hg = h / HG;
+    const int in_slot = (h % HG) * G + hq % G;       // row index inside a slot
+    const int ngroups = a.Hkv / HG;
     const int n = tiles_of(a.context_lens[b]);
     float* o = a.out + (size_t)row * D;
     if (n == 0) {
-        for (int d = tid; d < D; d += kMergeThreads)
+        for (int d = lane; d < D; d += kWave)
             o[d] = 0.f;
-        if (a.lse_out && tid == 0)
+        if (a.lse_out && lane == 0)
             a.lse_out[row] = -__builtin_inff();
         return;
     }
-    const long long N = ws.nwaves;
-    const long long total = tiles_before(a.context_lens, a.B) * a.Hkv;
-    const long long ustart = tiles_before(a.context_lens, b) * a.Hkv + (long long)h * n;
+    // tiles of all sequences and of the sequences before b, in one pass
+    long long total = 0, before = 0;
+    for (int c = 0; c < a.B; c += kWave) {
+        const int bb = c + lane;
+        const int nn = bb < a.B ? tiles_of(a.context_lens[bb]) : 0;
+        total += wave_sum_i(nn);
+        before += wave_sum_i(bb < b ? nn : 0);
+    }
+    total *= ngroups;
+    const long long R = ws.ngroups_launched;
+    const long long ustart = before * ngroups + (long long)hg * n;
     const long long ulast = ustart + n - 1;
-    auto wave_of = [&](long long x) {
-        long long w = x * N / total;
-        while (w + 1 < N && range_start(w + 1, total, N) <= x)
-            ++w;
-        while (w > 0 && range_start(w, total, N) > x)
-            --w;
-        return w;
+    auto range_of = [&](long long x) {
+        long long r = x * R / total;
+        while (r + 1 < R && range_start(r + 1, total, R) <= x)
+            ++r;
+        while (r > 0 && range_start(r, total, R) > x)
+            --r;
+        return r;
     };
-    const long long wf = wave_of(ustart);
-    const long long wl = wave_of(ulast);
-    if (wf == wl)
+    const long long rf = range_of(ustart);
+    const long long rl = range_of(ulast);
+    if (rf == rl)
         return;
-    // Waves between wf and wl with an empty range (fewer tiles than waves)
-    // hold no piece of this unit.
-    auto piece_slot = [&](long long w) -> long long {
-        const long long r0 = range_start(w, total, N);
-        if (range_start(w + 1, total, N) <= r0)
+    const int rows_per_slot = HG * G;
+    // Groups between rf and rl with an empty range (fewer tiles than
+    // groups) hold no piece of this unit.
+    auto piece_row = [&](long long r) -> long long {
+        const long long s0 = range_start(r, total, R);
+        if (range_start(r + 1, total, R) <= s0)
             return -1;
-        return 2 * w + ((w == wf && r0 < ustart) ? 1 : 0);
+        const long long slot = 2 * r + ((r == rf && s0 < ustart) ? 1 : 0);
+        return slot * rows_per_slot + in_slot;
     };
-    const int np = (int)(wl - wf + 1);
+    const int p0 = lane / cols;
+    const int col = lane % cols;
     float m = -__builtin_inff();
-    for (int i = tid; i < np; i += kMergeThreads) {
-        const long long slot = piece_slot(wf + i);
-        if (slot >= 0)
-            m = fmaxf(m, ws.part_lse[slot * G + g]);
+    for (long long r = rf + p0; r <= rl; r += npg) {
+        const long long pr = piece_row(r);
+        if (pr >= 0)
+            m = fmaxf(m, ws.part_lse[pr]);
     }
-    m = group_reduce(m, scratch, true);
+    m = wave_max(m);
     float wsum = 0.f;
-    for (int i = tid; i < np; i += kMergeThreads) {
-        const long long slot = piece_slot(wf + i);
-        const float wt = slot >= 0 ? __expf(ws.part_lse[slot * G + g] - m) : 0.f;
-        wts[i] = wt;
+    f32x4 accv = {0.f, 0.f, 0.f, 0.f};
+    for (long long r = rf + p0; r <= rl; r += npg) {
+        const long long pr = piece_row(r);
+        if (pr < 0)
+            continue;
+        const float wt = __expf(ws.part_lse[pr] - m);
         wsum += wt;
+        accv += wt * *(const f32x4*)(ws.part_out + pr * D + 4 * col);
     }
-    wsum = group_reduce(wsum, scratch, false);      // also orders the wts writes
-    constexpr int cols = D / 4;
-    constexpr int ng = kMergeThreads / cols;
-    const int col = tid % cols;
-    const int grp = tid / cols;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int i = grp; i < np; i += ng) {
-        const float wt = wts[i];
-        if (wt != 0.f) {
-            const long long slot = piece_slot(wf + i);
-            acc += wt * *(const f32x4*)(ws.part_out + ((size_t)slot * G + g) * D + 4 * col);
-        }
+#pragma unroll
+    for (int k = cols; k < kWave; k <<= 1) {
+        wsum += xor_shuffle(wsum, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            accv[e] += xor_shuffle(accv[e], k);
     }
-    __syncthreads();
-    red[tid] = acc;
-    __syncthreads();
-    if (tid < cols) {
-        f32x4 t = red[tid];
-        for (int k = 1; k < ng; ++k)
-            t += red[k * cols + tid];
-        *(f32x4*)(o + 4 * tid) = t * (1.0f / wsum);
-    }
-    if (a.lse_out && tid == 0)
+    if (lane < cols)
+        *(f32x4*)(o + 4 * col) = accv * (1.0f / wsum);
+    if (a.lse_out && lane == 0)
         a.lse_out[row] = m + __logf(wsum);
 }
 
 template <int D, int BS, int FP8>
-int balanced_occupancy()
+int balanced_occupancy(int head_group)
 {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks, reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8>),
-            kWavesPerGroup * kWave, 0) != hipSuccess)
+            head_group * kWave, (size_t)head_group * Cfg<D, FP8>::LDS_BYTES) != hipSuccess)
         return 0;
     return blocks;
 }
@@ -719,19 +721,18 @@ int balanced_occupancy()
 template <int D, int BS, int FP8>
 hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, hipStream_t stream)
 {
-    const long long groups = ((long long)ws.nwaves + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8>), dim3((unsigned)groups),
-                       dim3(kWavesPerGroup * kWave), 0, stream, a, ws);
+    const size_t lds = (size_t)ws.head_group * Cfg<D, FP8>::LDS_BYTES;
+    hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8>), dim3((unsigned)ws.ngroups_launched),
+                       dim3(ws.head_group * kWave), lds, stream, a, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     const long long rows = (long long)a.B * a.Hq;
-    if (rows > 0x7FFFFFFFLL)
+    const long long groups = (rows + kMergeWaves - 1) / kMergeWaves;
+    if (groups > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
-    // a unit has at most nwaves + 1 pieces (one per wave plus an empty-range gap)
-    const size_t lds = kMergeThreads * sizeof(f32x4) + ((size_t)ws.nwaves + 1) * sizeof(float);
-    hipLaunchKernelGGL((balanced_merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads),
-                       lds, stream, a, ws);
+    hipLaunchKernelGGL((balanced_merge_kernel<D>), dim3((unsigned)groups),
+                       dim3(kMergeWaves * kWave), 0, stream, a, ws);
     return hipGetLastError();
 }
 
@@ -762,16 +763,20 @@ hipError_t launch_d_bs(const DecodeArgs& a, int kv_dtype, hipStream_t stream)
 
 } // namespace
 
-int decode_waves_per_group()
+int balanced_head_group(int Hkv)
 {
-    return kWavesPerGroup;
+    for (int hg = kMaxHeadGroup; hg > 1; --hg)
+        if (Hkv % hg == 0)
+            return hg;
+    return 1;
 }
 
-int balanced_blocks_per_cu(int D, int block_size, int kv_dtype)
+int balanced_groups_per_cu(int D, int block_size, int kv_dtype, int head_group)
 {
 #define PKV_OCC(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1>() : balanced_occupancy<d, bs, 0>();
+        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1>(head_group)                \
+                             : balanced_occupancy<d, bs, 0>(head_group);
     PKV_OCC(128, 16)
     PKV_OCC(128, 32)
     PKV_OCC(64, 16)

@@ -35,12 +35,13 @@ struct DecodeArgs {
     float scale_log2;     // softmax scale * log2(e)
 };
 
-// Workspace of the balanced decode: 2 partial slots per wave, each with
-// G rows of D floats and G lse values.
+// Workspace of the balanced decode: 2 partial slots per launched
+// work-group, each with head_group * G rows of D floats and as many lse.
 struct BalanceArgs {
-    float* part_out;      // [2 * nwaves, G, D]
-    float* part_lse;      // [2 * nwaves, G]
-    int32_t nwaves;
+    float* part_out;          // [2 * ngroups_launched, head_group * G, D]
+    float* part_lse;          // [2 * ngroups_launched, head_group * G]
+    int32_t ngroups_launched; // work-groups (token ranges) of the decode launch
+    int32_t head_group;       // kv heads per work-group (divides Hkv, <= 8)
 };
 
 struct ReduceArgs {
@@ -58,9 +59,9 @@ hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtyp
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
                                   int block_size, int kv_dtype, hipStream_t stream);
-// resident work-groups per compute unit of the balanced kernel (0 on error)
-int balanced_blocks_per_cu(int D, int block_size, int kv_dtype);
-// waves per work-group of the decode kernels
-int decode_waves_per_group();
+// kv heads per work-group of the balanced decode for Hkv kv heads
+int balanced_head_group(int Hkv);
+// resident work-groups per compute unit of the balanced decode (0 on error)
+int balanced_groups_per_cu(int D, int block_size, int kv_dtype, int head_group);
 
 } // namespace pkv
