@@ -1,15 +1,18 @@
 """Throughput of one decode step of paged attention on one MI355X.
 
 A step is one pass of the whole hot path over one batch: append the new
-token's K/V (paged_kv_append), split-context paged decode attention
-(paged_decode_attention) and the log-sum-exp merge (split_context_reduce).
-Inputs are seeded synthetic arrays already resident in HBM.
+token's K/V to every cache group (paged_kv_append), then, for every logical
+layer, decode attention over that layer's group cache -- work-balanced
+(paged_decode_attention_balanced, which merges cut units itself) or fixed
+splits (paged_decode_attention + split_context_reduce).  Single-layer
+workloads have one layer and one group; the fp8 workload has 36 layers over
+9 groups.  Inputs are seeded synthetic arrays already resident in HBM.
 
 Prints ONE JSON line.  value = KV-read GB/s of the whole step (ideal KV
-bytes 2 * sum(ctx) * Hkv * D * bytes_per_elem per step / step time).
-roofline = the attention kernel alone, timed with HIP events on the stream
-it is launched on.  cpu_baseline = the CPU oracle on a bounded sample of the
-same workload, on this machine's host cores.
+bytes 2 * sum(ctx) * Hkv * D * bytes_per_elem per layer call, times the
+layers, / step time).  roofline = one attention call, timed with HIP events
+on the stream it is launched on.  cpu_baseline = the CPU oracle on a bounded
+sample of the same workload, on this machine's host cores.
 """
 from __future__ import annotations
 
@@ -72,8 +75,7 @@ def main():
         S = a.split if a.split is not None else (wl.split_tokens or 512)
     dev = torch.device("cuda:0")
     t_gen = time.time()
-    groups = [0] if wl.kv_dtype == "bf16" else [0]
-    inp = generate(wl, groups=groups)
+    inp = generate(wl)                    # every cache group of the workload
     print(f"bench: generated {wl.name} in {time.time() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
 
@@ -83,58 +85,68 @@ def main():
             x = x.view(np.int16)
         return torch.from_numpy(x).to(dev)
 
-    ks = vs = None
-    if wl.kv_dtype == "fp8":
-        # fp8 cache built on the device from the bf16 source values
-        # (input preparation only: amax / 448 per block and kv head)
-        def quant(src):
-            x = up(src).view(torch.bfloat16).float()
-            live = torch.from_numpy(
-                np.arange(wl.block_size)[None, :] < inp.live[:, None]).to(dev)
-            xm = torch.where(live[:, :, None, None] & torch.isfinite(x), x.abs(),
-                             torch.zeros_like(x))
-            amax = xm.amax(dim=(1, 3))
-            sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
-            y = (x / sc[:, None, :, None]).clamp(-448, 448)
-            return y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
+    live = torch.from_numpy(np.arange(wl.block_size)[None, :] < inp.live[:, None]).to(dev)
 
-        k, ks = quant(inp.k_pool[0])
-        v, vs = quant(inp.v_pool[0])
-    else:
-        k, v = up(inp.k_pool[0]), up(inp.v_pool[0])
-    kn, vn = up(inp.k_new[0]), up(inp.v_new[0])
-    q = up(inp.query[0])
+    def quant(src):
+        # fp8 cache built on the device from the bf16 source values (input
+        # preparation only: scale = amax / 448 per block and kv head)
+        x = up(src).view(torch.bfloat16).float()
+        xm = torch.where(live[:, :, None, None] & torch.isfinite(x), x.abs(), torch.zeros_like(x))
+        amax = xm.amax(dim=(1, 3))
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
+        y = (x / sc[:, None, :, None]).clamp(-448, 448)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
+
+    # one cache per layer group ([A] cross-layer KV sharing: layer l reads
+    # group l // layers_per_group); bf16 workloads have a single group
+    caches = []
+    for g in range(wl.groups):
+        if wl.kv_dtype == "fp8":
+            k, ks = quant(inp.k_pool[g])
+            v, vs = quant(inp.v_pool[g])
+        else:
+            k, v, ks, vs = up(inp.k_pool[g]), up(inp.v_pool[g]), None, None
+        caches.append((k, v, ks, vs, up(inp.k_new[g]), up(inp.v_new[g])))
+    qs = [up(inp.query[l]) for l in range(wl.layers)]
     bt, cl = up(inp.block_tables), up(inp.context_lens)
     ctx = inp.context_lens.astype(np.int64)
-    ideal = 2 * int(ctx.sum()) * wl.Hkv * wl.D * wl.bytes_per_elem
+    per_layer = 2 * int(ctx.sum()) * wl.Hkv * wl.D * wl.bytes_per_elem
+    ideal = per_layer * wl.layers
     scale = float(inp.scale)
 
     ms = pkv.max_splits_for(int(ctx.max()), S) if S else 1
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     po = torch.empty((wl.B, wl.Hq, ms, wl.D), dtype=torch.float32, device=dev) if S else None
     pl = torch.empty((wl.B, wl.Hq, ms), dtype=torch.float32, device=dev) if S else None
-    ws = pkv.make_workspace(q, k) if mode == "balanced" else None
+    ws = pkv.make_workspace(qs[0], caches[0][0]) if mode == "balanced" else None
 
-    ev = []  # (start, end) around each attention launch in the timed region
+    ev = []  # (start, end) around each attention call in the timed region
 
     def step(record):
-        pkv.paged_kv_append(kn, vn, k, v, bt, cl, k_scale=ks, v_scale=vs)
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        if mode == "split":
-            pkv.paged_decode_attention(q, k, v, bt, cl, scale, split_tokens=S, partial_out=po,
-                                       partial_lse=pl, k_scale=ks, v_scale=vs)
-        elif mode == "balanced":
-            pkv.paged_decode_attention_balanced(q, k, v, bt, cl, scale, workspace=ws, out=out,
-                                                k_scale=ks, v_scale=vs)
-        else:
-            pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks, v_scale=vs)
-        if record:
-            e1.record()
-            ev.append((e0, e1))
-        if mode == "split":
-            pkv.split_context_reduce(po, pl, cl, S, out=out)
+        for k, v, ks, vs, kn, vn in caches:
+            pkv.paged_kv_append(kn, vn, k, v, bt, cl, k_scale=ks, v_scale=vs)
+        for layer in range(wl.layers):
+            k, v, ks, vs, _, _ = caches[layer // wl.layers_per_group]
+            q = qs[layer]
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            if mode == "split":
+                pkv.paged_decode_attention(q, k, v, bt, cl, scale, split_tokens=S,
+                                           partial_out=po, partial_lse=pl, k_scale=ks,
+                                           v_scale=vs)
+            elif mode == "balanced":
+                pkv.paged_decode_attention_balanced(q, k, v, bt, cl, scale, workspace=ws,
+                                                    out=out, k_scale=ks, v_scale=vs)
+            else:
+                pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks,
+                                           v_scale=vs)
+            if record:
+                e1.record()
+                ev.append((e0, e1))
+            if mode == "split":
+                pkv.split_context_reduce(po, pl, cl, S, out=out)
 
     if a.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -155,7 +167,7 @@ def main():
 
     step_s = wall / a.steps
     gbs = ideal / step_s / 1e9
-    kern_gbs = ideal / kern_s / 1e9
+    kern_gbs = per_layer / kern_s / 1e9
     traffic = _measured_traffic(a.traffic_json, f"{wl.name}:{mode}")
 
     cpu = None
@@ -183,6 +195,7 @@ def main():
             "ctx_sum": int(ctx.sum()), "ctx_mean": round(float(ctx.mean()), 1),
             "ctx_min": int(ctx.min()), "ctx_max": int(ctx.max()), "schedule": mode,
             "split_tokens": S, "num_blocks": inp.num_blocks, "ideal_kv_bytes_per_step": ideal,
+            "layers_per_step": wl.layers, "cache_groups": wl.groups,
             "step": {"split": "paged_kv_append + paged_decode_attention(split) + "
                               "split_context_reduce",
                      "balanced": "paged_kv_append + paged_decode_attention_balanced "
@@ -195,7 +208,7 @@ def main():
                        "balanced": "decode_balanced_kernel + balanced_merge_kernel"}[mode],
             "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": ideal,
+            "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": per_layer,
         },
         "cpu_baseline": cpu,
     }

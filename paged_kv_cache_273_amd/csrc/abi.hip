@@ -30,9 +30,27 @@ int launched(hipError_t e)
 }
 
 constexpr int32_t kMaxGroup = 16;     // query heads per kv head (one MFMA column tile)
+// MI355X last-level (Infinity Cache / MALL) capacity.  A K+V pool that fits
+// may be re-read from it by the next call; larger pools are streamed.
+constexpr int64_t kMallBytes = (int64_t)256 << 20;
 constexpr int32_t kMaxSplits = 15360; // reduce keeps one weight per split in LDS
 // per-sequence token bound of the balanced path (64-sequence tile sums stay in int32)
 constexpr int64_t kMaxTokens = (int64_t)1 << 25;
+
+// Load policy of the decode kernels: non-temporal (streaming) unless the
+// whole K+V pool fits the MALL.  PKV_FORCE_LOAD_POLICY (0 = default
+// policy, 1 = non-temporal) pins it at build time for measurements.
+bool stream_kv_loads(int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D,
+                     int32_t kv_dtype)
+{
+#ifdef PKV_FORCE_LOAD_POLICY
+    return PKV_FORCE_LOAD_POLICY != 0;
+#else
+    const int64_t esize = kv_dtype == PKV_FP8_E4M3 ? 1 : 2;
+    const int64_t pool = 2 * (int64_t)num_blocks * block_size * Hkv * D * esize;
+    return pool > kMallBytes;
+#endif
+}
 
 } // namespace
 
@@ -143,7 +161,8 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     a.split_tokens = split_tokens;
     a.max_splits = split_tokens > 0 ? max_splits : 1;
     a.scale_log2 = scale * 1.4426950408889634f;
-    return launched(pkv::launch_decode(a, D, block_size, kv_dtype, (hipStream_t)stream));
+    const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
+    return launched(pkv::launch_decode(a, D, block_size, kv_dtype, nt, (hipStream_t)stream));
 }
 
 // Work-groups of the balanced decode on the current device: exactly the
@@ -240,7 +259,14 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     ws.ngroups_launched = n;
     ws.part_out = (float*)workspace;
     ws.part_lse = ws.part_out + (size_t)2 * n * ws.head_group * G * D;
-    return launched(pkv::launch_decode_balanced(a, ws, D, block_size, kv_dtype,
+    // range boundaries are computed in double precision: keep
+    // (tiles of the call) * (groups launched) below 2^52
+    const int64_t ngroups = Hkv / ws.head_group;
+    const int64_t max_tiles = (int64_t)B * (((int64_t)max_blocks * block_size + 31) / 32) * ngroups;
+    if (max_tiles * ((int64_t)n + 1) >= ((int64_t)1 << 52))
+        return PKV_EUNSUPPORTED;
+    const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
+    return launched(pkv::launch_decode_balanced(a, ws, D, block_size, kv_dtype, nt,
                                                 (hipStream_t)stream));
 }
 

@@ -60,18 +60,20 @@ constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 #endif
 constexpr int kTile = 32;
 
-// K/V loads carry the non-temporal hint: every cached byte is read once
-// per decode step, and as streaming requests the L2 neither stalls on tag
-// allocation nor runs out of DRAM request credits (rocprofv3: TCC tag and
-// DRAM-credit stalls fall ~60x and the 8B-shape decode runs ~1.9x faster
-// than with default-policy loads).
-__device__ __forceinline__ u32x4 load_stream(const unsigned char* p)
+// K/V loads, with or without the non-temporal hint.  A cache much larger
+// than the 256 MB MALL is read once per call and should stream (NT = 1):
+// as streaming requests the L2 neither stalls on tag allocation nor runs
+// out of DRAM request credits (rocprofv3: TCC tag and DRAM-credit stalls
+// fall ~60x and the 8B-shape decode runs ~1.9x faster than with
+// default-policy loads).  A cache that fits the MALL may be re-read by the
+// next call (layers sharing one cache) and keeps the default policy
+// (NT = 0), which lets those re-reads hit.
+template <int NT>
+__device__ __forceinline__ u32x4 load_kv(const unsigned char* p)
 {
-#ifdef PKV_TEMPORAL_LOADS
+    if (NT)
+        return __builtin_nontemporal_load((const u32x4*)p);
     return *(const u32x4*)p;
-#else
-    return __builtin_nontemporal_load((const u32x4*)p);
-#endif
 }
 
 template <int D, int FP8>
@@ -130,7 +132,7 @@ struct RangeAcc {
 
 // One wave attends the G query heads of kv head h of sequence b over the
 // logical tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.
-template <int D, int BS, int FP8>
+template <int D, int BS, int FP8, int NT>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
                                              int h, int t_begin, int t_end, RangeAcc<D>& r)
 {
@@ -217,7 +219,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             const unsigned char* blk = kc + (size_t)(tau ? ta.pB : ta.pA) * blk_stride;
 #pragma unroll
             for (int c = 0; c < C::K_LOADS; ++c)
-                tl.k[tau][c] = load_stream(blk + k_off[tau] + 64 * c);
+                tl.k[tau][c] = load_kv<NT>(blk + k_off[tau] + 64 * c);
         }
     };
     auto load_v = [&](const TileAddr& ta, Tile<D, FP8>& tl) {
@@ -225,7 +227,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         for (int k = 0; k < C::V_LOADS; ++k) {
             const int p = (BS == 16 && k * C::V_RPI >= 16) ? ta.pB : ta.pA;
             const unsigned char* blk = vc + (size_t)p * blk_stride;
-            tl.v[k] = load_stream(blk + v_off[k]);
+            tl.v[k] = load_kv<NT>(blk + v_off[k]);
         }
     };
 
@@ -414,7 +416,7 @@ __device__ __forceinline__ void store_empty_row(float* o)
 
 // Fixed partition: one wave per (b, h) over the whole context, or per
 // (b, h, split) over [s * split_tokens, min(T, (s + 1) * split_tokens)).
-template <int D, int BS, int FP8, bool SPLIT>
+template <int D, int BS, int FP8, int NT, bool SPLIT>
 __global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_kernel(DecodeArgs a)
 {
@@ -454,7 +456,7 @@ void decode_kernel(DecodeArgs a)
         return;
     }
     RangeAcc<D> r;
-    attend_range<D, BS, FP8>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin, t_end, r);
+    attend_range<D, BS, FP8, NT>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin, t_end, r);
     float inv, lse;
     finish_range<D>(r, inv, lse);
     if (!live_col)
@@ -529,12 +531,16 @@ __device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int ngrou
     before_out = base;
 }
 
+// floor(r * total / R).  Exact while r * total < 2^52 (checked on the
+// host): the double quotient of two exactly represented integers cannot
+// cross the integer above the true quotient, whose distance is >= 1/R.
+// (A 64-bit integer division is a long software sequence on the GPU.)
 __device__ __forceinline__ long long range_start(long long r, long long total, long long R)
 {
-    return r * total / R;
+    return (long long)__builtin_floor((double)(r * total) / (double)R);
 }
 
-template <int D, int BS, int FP8>
+template <int D, int BS, int FP8, int NT>
 __global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 {
@@ -572,7 +578,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         const int t_end = min(T, (int)(pend - ustart) * kTile);
         const int h = hg * HG + wave;
         RangeAcc<D> acc;
-        attend_range<D, BS, FP8>(a, lds, b, h, t_begin, t_end, acc);
+        attend_range<D, BS, FP8, NT>(a, lds, b, h, t_begin, t_end, acc);
         float inv, lse;
         finish_range<D>(acc, inv, lse);
         if (r16 < G) {
@@ -609,8 +615,8 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 // (b, head group of hq) when several work-groups shared it, writes zeros /
 // -inf for an empty sequence, and leaves rows that one group finished
 // alone untouched.  Lane (p, c) owns four output elements (column c) and
-// every npg-th piece starting at p, so all pieces' loads are in flight
-// together; the npg partial sums meet through lane butterflies.
+// every npg-th piece starting at p; the npg partial sums meet through
+// lane butterflies.
 constexpr int kMergeWaves = 4;
 
 template <int D>
@@ -654,7 +660,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     const long long ustart = before * ngroups + (long long)hg * n;
     const long long ulast = ustart + n - 1;
     auto range_of = [&](long long x) {
-        long long r = x * R / total;
+        long long r = (long long)((double)x * (double)R / (double)total);
         while (r + 1 < R && range_start(r + 1, total, R) <= x)
             ++r;
         while (r > 0 && range_start(r, total, R) > x)
@@ -677,23 +683,54 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     };
     const int p0 = lane / cols;
     const int col = lane % cols;
+    // one online pass (running max, rescaled sums) over this lane's
+    // pieces, four pieces' loads in flight per step
+    constexpr int kBatch = 4;
     float m = -__builtin_inff();
-    for (long long r = rf + p0; r <= rl; r += npg) {
-        const long long pr = piece_row(r);
-        if (pr >= 0)
-            m = fmaxf(m, ws.part_lse[pr]);
-    }
-    m = wave_max(m);
     float wsum = 0.f;
     f32x4 accv = {0.f, 0.f, 0.f, 0.f};
-    for (long long r = rf + p0; r <= rl; r += npg) {
-        const long long pr = piece_row(r);
-        if (pr < 0)
+    for (long long base = rf + p0; base <= rl; base += kBatch * npg) {
+        long long pr[kBatch];
+        float l[kBatch];
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const long long r = base + (long long)k * npg;
+            pr[k] = r <= rl ? piece_row(r) : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            l[k] = -__builtin_inff();
+            v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (pr[k] >= 0) {
+                l[k] = ws.part_lse[pr[k]];
+                v[k] = *(const f32x4*)(ws.part_out + pr[k] * D + 4 * col);
+            }
+        }
+        float mb = l[0];
+#pragma unroll
+        for (int k = 1; k < kBatch; ++k)
+            mb = fmaxf(mb, l[k]);
+        const float m_new = fmaxf(m, mb);
+        if (m_new == -__builtin_inff())
             continue;
-        const float wt = __expf(ws.part_lse[pr] - m);
-        wsum += wt;
-        accv += wt * *(const f32x4*)(ws.part_out + pr * D + 4 * col);
+        const float sc = __expf(m - m_new);
+        wsum *= sc;
+        accv *= sc;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const float wt = __expf(l[k] - m_new);
+            wsum += wt;
+            accv += wt * v[k];
+        }
+        m = m_new;
     }
+    // bring the npg lane groups of a column to a common max, then add them
+    const float mrow = wave_max(m);
+    const float f = __expf(m - mrow);
+    wsum *= f;
+    accv *= f;
+    m = mrow;
 #pragma unroll
     for (int k = cols; k < kWave; k <<= 1) {
         wsum += xor_shuffle(wsum, k);
@@ -712,18 +749,24 @@ int balanced_occupancy(int head_group)
 {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8>),
+            &blocks, reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8, 1>),
             head_group * kWave, (size_t)head_group * Cfg<D, FP8>::LDS_BYTES) != hipSuccess)
         return 0;
     return blocks;
 }
 
 template <int D, int BS, int FP8>
-hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, hipStream_t stream)
+hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt,
+                             hipStream_t stream)
 {
     const size_t lds = (size_t)ws.head_group * Cfg<D, FP8>::LDS_BYTES;
-    hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8>), dim3((unsigned)ws.ngroups_launched),
-                       dim3(ws.head_group * kWave), lds, stream, a, ws);
+    const dim3 grid((unsigned)ws.ngroups_launched), block(ws.head_group * kWave);
+    if (nt)
+        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 1>), grid, block, lds, stream, a,
+                           ws);
+    else
+        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 0>), grid, block, lds, stream, a,
+                           ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -736,8 +779,8 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, hipStre
     return hipGetLastError();
 }
 
-template <int D, int BS, int FP8>
-hipError_t launch_d_bs_dt(const DecodeArgs& a, hipStream_t stream)
+template <int D, int BS, int FP8, int NT>
+hipError_t launch_fixed_t(const DecodeArgs& a, hipStream_t stream)
 {
     const bool split = a.split_tokens > 0;
     const long long units = (long long)a.B * a.Hkv * (split ? a.max_splits : 1);
@@ -748,17 +791,16 @@ hipError_t launch_d_bs_dt(const DecodeArgs& a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)groups), block(kWavesPerGroup * kWave);
     if (split)
-        hipLaunchKernelGGL((decode_kernel<D, BS, FP8, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, FP8, NT, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, BS, FP8, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, FP8, NT, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, int BS>
-hipError_t launch_d_bs(const DecodeArgs& a, int kv_dtype, hipStream_t stream)
+template <int D, int BS, int FP8>
+hipError_t launch_fixed_d_bs_dt(const DecodeArgs& a, bool nt, hipStream_t stream)
 {
-    return kv_dtype == 1 ? launch_d_bs_dt<D, BS, 1>(a, stream)
-                         : launch_d_bs_dt<D, BS, 0>(a, stream);
+    return nt ? launch_fixed_t<D, BS, FP8, 1>(a, stream) : launch_fixed_t<D, BS, FP8, 0>(a, stream);
 }
 
 } // namespace
@@ -786,12 +828,12 @@ int balanced_groups_per_cu(int D, int block_size, int kv_dtype, int head_group)
 }
 
 hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
-                                  int block_size, int kv_dtype, hipStream_t stream)
+                                  int block_size, int kv_dtype, bool nt, hipStream_t stream)
 {
 #define PKV_BAL(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1>(a, ws, stream)              \
-                             : launch_balanced_t<d, bs, 0>(a, ws, stream);
+        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1>(a, ws, nt, stream)          \
+                             : launch_balanced_t<d, bs, 0>(a, ws, nt, stream);
     PKV_BAL(128, 16)
     PKV_BAL(128, 32)
     PKV_BAL(64, 16)
@@ -800,14 +842,19 @@ hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, in
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype,
+hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype, bool nt,
                          hipStream_t stream)
 {
-    if (D == 128)
-        return block_size == 16 ? launch_d_bs<128, 16>(a, kv_dtype, stream)
-                                : launch_d_bs<128, 32>(a, kv_dtype, stream);
-    return block_size == 16 ? launch_d_bs<64, 16>(a, kv_dtype, stream)
-                            : launch_d_bs<64, 32>(a, kv_dtype, stream);
+#define PKV_FIX(d, bs)                                                                  \
+    if (D == d && block_size == bs)                                                    \
+        return kv_dtype == 1 ? launch_fixed_d_bs_dt<d, bs, 1>(a, nt, stream)           \
+                             : launch_fixed_d_bs_dt<d, bs, 0>(a, nt, stream);
+    PKV_FIX(128, 16)
+    PKV_FIX(128, 32)
+    PKV_FIX(64, 16)
+    PKV_FIX(64, 32)
+#undef PKV_FIX
+    return hipErrorInvalidValue;
 }
 
 } // namespace pkv

@@ -54,11 +54,12 @@ struct ReduceArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype,
+// nt: stream the K/V loads with the non-temporal hint
+hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype, bool nt,
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
-                                  int block_size, int kv_dtype, hipStream_t stream);
+                                  int block_size, int kv_dtype, bool nt, hipStream_t stream);
 // kv heads per work-group of the balanced decode for Hkv kv heads
 int balanced_head_group(int Hkv);
 // resident work-groups per compute unit of the balanced decode (0 on error)
