@@ -65,9 +65,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 // One 256-thread work-group per (b, hq).  Threads first take the live
 // splits' lse values (M = max, w_s = exp(lse_s - M), W = sum w_s) and park
 // w_s in LDS; then thread (group g, column c) sums w_s * o_s over the
-// splits s = g, g + NG, ... for four output elements, so a work-group keeps
-// NG independent 16-byte loads per column in flight; the NG partial sums
-// meet in LDS.
+// splits s = g, g + NG, ... for four output elements, four splits' loads
+// at a time; the NG partial sums meet in LDS.
 constexpr int kReduceThreads = 256;
 
 __device__ __forceinline__ float block_reduce(float v, float* scratch, bool is_max)
@@ -123,10 +122,22 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a)
     const int grp = tid / cols;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (grp < ng) {
-        for (int s = grp; s < ns; s += ng) {
-            const float w = w_lds[s];
-            if (w != 0.f)
-                acc += w * *(const f32x4*)(po + (size_t)s * a.D + 4 * col);
+        // four splits' loads in flight per step
+        constexpr int kBatch = 4;
+        for (int s0 = grp; s0 < ns; s0 += kBatch * ng) {
+            f32x4 v[kBatch];
+            float w[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int s = s0 + k * ng;
+                w[k] = s < ns ? w_lds[s] : 0.f;
+                v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (w[k] != 0.f)
+                    v[k] = *(const f32x4*)(po + (size_t)s * a.D + 4 * col);
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                acc += w[k] * v[k];
         }
     }
     __syncthreads();
