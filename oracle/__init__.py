@@ -64,6 +64,10 @@ def lib():
         "orc_split_reduce": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
         "orc_fp8_block_scales": (None, [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
         "orc_fp8_quantize_pool": (None, [_P, _P, _I32, _I32, _I32, _I32, _P]),
+        "orc_write_tokens": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                    _I32, _I32, _I32]),
+        "orc_multiquery_attention": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                            _I32, _I32, _I32, _I32, _F64, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -212,3 +216,36 @@ def fp8_quantize_pool(src_pool, scales):
     codes = np.empty(src_pool.shape, dtype=np.uint8)
     lib().orc_fp8_quantize_pool(_ptr(src_pool), _ptr(scales), nb, bs, Hkv, D, _ptr(codes))
     return codes
+
+
+# ---------------------------------------------------------------- several new tokens
+def write_tokens(k_rows, v_rows, query_start, k_cache, v_cache, block_tables, context_lens,
+                 block_size, kv_dtype="bf16", k_scale=None, v_scale=None) -> None:
+    """In-place write of each sequence's q_b new K/V rows ([total_rows, Hkv, D])
+    into the positions T_b - q_b .. T_b - 1 of host copies of the pools."""
+    total, Hkv, D = k_rows.shape
+    B = context_lens.shape[0]
+    rc = lib().orc_write_tokens(_ptr(k_rows), _ptr(v_rows), _ptr(query_start), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                B, Hkv, D, block_size, _DT[kv_dtype])
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+
+
+def multiquery_attention(query, query_start, k_cache, v_cache, block_tables, context_lens,
+                         scale, *, block_size, Hkv, kv_dtype="bf16", k_scale=None,
+                         v_scale=None):
+    """Causal multi-query oracle: (out [total_rows, Hq, D], lse [total_rows, Hq])."""
+    total, Hq, D = query.shape
+    B = context_lens.shape[0]
+    out = np.empty((total, Hq, D), dtype=np.float64)
+    lse = np.empty((total, Hq), dtype=np.float64)
+    rc = lib().orc_multiquery_attention(_ptr(query), _ptr(query_start), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                        _ptr(block_tables), block_tables.shape[1],
+                                        _ptr(context_lens), B, Hq, Hkv, D, block_size,
+                                        _DT[kv_dtype], float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out, lse

@@ -26,7 +26,11 @@
  *   - FP8 is OCP E4M3FN (bias 7, max finite 448, NaN = S.1111.111, no
  *     infinities), round-to-nearest-even, saturating to +-448;
  *   - split-context partials are normalised outputs plus natural-log
- *     log-sum-exp values; an empty split has lse = -inf and is ignored.
+ *     log-sum-exp values; an empty split has lse = -inf and is ignored;
+ *   - several new tokens of one sequence (a prefill chunk, or draft tokens
+ *     under verification) are its last q_b positions; new token i sits at
+ *     position T_b - q_b + i and attends causally over [0, that position];
+ *     fp8 writes use the block's existing scale and saturate.
  *
  * Parity pins for every function live in tests/ (marked "not gpu").
  */
@@ -451,6 +455,98 @@ int32_t orc_split_reduce(const float* partial_out, const float* partial_lse,
     }
     free(po);
     free(pl);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Several new tokens per sequence (chunked prefill, speculative verify). */
+/* [B] "Continuous Batching": chunked prefill feeds a long prompt in      */
+/* pieces of several tokens; [A] "How does speculative decoding interact  */
+/* with KV-cache compression": the target verifies several draft tokens   */
+/* at once.  Sequence b brings q_b = query_start[b+1] - query_start[b]     */
+/* new tokens, the last q_b positions of its context_lens[b] tokens: row  */
+/* query_start[b] + i is position p = T_b - q_b + i.  Rows are            */
+/* [total_rows, H, D] with H = Hkv for K/V rows, Hq for queries/outputs.  */
+/* ------------------------------------------------------------------ */
+
+/* Writes the new tokens' K and V rows into their slots (the single-token
+ * append is the case q_b = 1).  Returns 0, or -1 if some q_b > T_b. */
+int32_t orc_write_tokens(const uint16_t* k_rows, const uint16_t* v_rows,
+                         const int32_t* query_start, void* k_cache, void* v_cache,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t B, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t kv_dtype)
+{
+    int32_t b, i, h, d;
+    for (b = 0; b < B; ++b) {
+        int32_t T = context_lens[b];
+        int32_t q = query_start[b + 1] - query_start[b];
+        if (q > T || q < 0)
+            return -1;
+        for (i = 0; i < q; ++i) {
+            int64_t row = query_start[b] + i;
+            int32_t t = T - q + i;
+            int32_t phys = block_tables[(int64_t)b * max_blocks + t / block_size];
+            int32_t slot = t % block_size;
+            for (h = 0; h < Hkv; ++h)
+                for (d = 0; d < D; ++d) {
+                    int64_t src = (row * Hkv + h) * D + d;
+                    int64_t dst = pool_index(phys, slot, h, d, block_size, Hkv, D);
+                    if (kv_dtype == 0) {
+                        ((uint16_t*)k_cache)[dst] = k_rows[src];
+                        ((uint16_t*)v_cache)[dst] = v_rows[src];
+                    } else {
+                        ((uint8_t*)k_cache)[dst] =
+                            orc_e4m3_quantize(k_rows[src], k_scale[(int64_t)phys * Hkv + h]);
+                        ((uint8_t*)v_cache)[dst] =
+                            orc_e4m3_quantize(v_rows[src], v_scale[(int64_t)phys * Hkv + h]);
+                    }
+                }
+        }
+    }
+    return 0;
+}
+
+/* Causal attention of every new token: row query_start[b] + i (position
+ * p = T_b - q_b + i) attends over tokens [0, p] of sequence b, each query
+ * head through its kv head as in the single-token case.  out
+ * [total_rows, Hq, D] and lse [total_rows, Hq].  Each row is the
+ * single-query attention of that row over the first p + 1 tokens.
+ * Returns 0, or -1 on bad arguments. */
+int32_t orc_multiquery_attention(const uint16_t* query, const int32_t* query_start,
+                                 const void* k_cache, const void* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype,
+                                 double scale, double* out, double* lse)
+{
+    int32_t b, i, hq;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || block_size <= 0
+        || (kv_dtype != 0 && kv_dtype != 1))
+        return -1;
+    for (b = 0; b < B; ++b) {
+        int32_t T = context_lens[b];
+        int32_t q = query_start[b + 1] - query_start[b];
+        const int32_t* table_row = block_tables + (int64_t)b * max_blocks;
+        if (q > T || q < 0)
+            return -1;
+        for (i = 0; i < q; ++i) {
+            int64_t row = query_start[b] + i;
+            int32_t p = T - q + i;
+            /* the row as a one-sequence batch: query [1, Hq, D], table [1, max_blocks] */
+            const uint16_t* qrow = query + row * Hq * D;
+            for (hq = 0; hq < Hq; ++hq) {
+                double l = orc_attend_range(qrow, k_cache, v_cache, k_scale, v_scale,
+                                            table_row, max_blocks, Hq, Hkv, D, block_size,
+                                            kv_dtype, scale, 0, hq, 0, p + 1,
+                                            out + (row * Hq + hq) * D);
+                if (lse)
+                    lse[row * Hq + hq] = l;
+            }
+        }
+    }
     return 0;
 }
 

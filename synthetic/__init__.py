@@ -9,9 +9,11 @@ from .workloads import (  # noqa: F401
     WORKLOADS,
     Workload,
     PagedInputs,
+    MultiQueryInputs,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
     generate,
+    generate_multiquery,
     make_workload,
     random_partials,
 )

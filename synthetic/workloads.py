@@ -26,6 +26,14 @@ Recipe (the same for every workload):
     hole or tail slot, produces NaN.
   * Appended token: k_new, v_new [B, Hkv, D], fresh N(0, 1) bf16 draws.
 
+Several new tokens per sequence (generate_multiquery): sequence b brings
+q_b new tokens, the last q_b of its T_b (chunked prefill, [B] "Continuous
+Batching"; the target's verification of draft tokens, [A] "How does
+speculative decoding interact with KV-cache compression").  q_b is drawn
+uniformly from the workload's q range and clipped to T_b; the q_b write
+slots hold NaN before the write; K/V rows [rows, Hkv, D] and query rows
+[layers, rows, Hq, D] are fresh draws with the same distributions.
+
 Nothing here computes attention, quantises, or merges; the fp8 workload
 carries bf16 source values, and each consumer quantises them with its own
 encoder.
@@ -45,6 +53,7 @@ _CHUNK = 1 << 22
 
 # stream ids
 _S_CTX, _S_PERM, _S_K, _S_V, _S_Q, _S_KNEW, _S_VNEW, _S_PART = range(1, 9)
+_S_QLEN, _S_KROWS, _S_VROWS, _S_QROWS = range(9, 13)
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
@@ -104,6 +113,7 @@ class Workload:
     split_tokens: int = 0             # 0: single pass
     layers: int = 1                   # logical layers per decode step
     layers_per_group: int = 1         # consecutive layers sharing one cache
+    q_uniform: Tuple[int, int] = (1, 1)  # new tokens per sequence (multi-query)
     seed: int = 273000
 
     @property
@@ -137,6 +147,14 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("llama70b_b4_ctx32k_split512_prefix2k", B=4, Hq=64, Hkv=8, D=128,
                  block_size=16, max_blocks=2048, ctx_fixed=(32768,) * 4, pool="exact",
                  shared_prefix_blocks=128, split_tokens=512, seed=273003),
+        # several new tokens per sequence: ragged 1..17 (tiny, oracle-sized)
+        Workload("tiny_mq_b4_hq8_hkv2_d64_bs16", B=4, Hq=8, Hkv=2, D=64, block_size=16,
+                 max_blocks=33, ctx_fixed=(1, 17, 100, 513), pool="fixed:64",
+                 q_uniform=(1, 17), seed=273010),
+        # verification of 4 draft tokens per sequence on the 70B ragged batch
+        Workload("llama70b_b64_ragged1k_16k_bs32_verify4", B=64, Hq=64, Hkv=8, D=128,
+                 block_size=32, max_blocks=512, ctx_uniform=(1024, 16384),
+                 pool="holes10", q_uniform=(4, 4), seed=273002),
         # fp8 cache, 36 layers in 9 groups of 4 sharing one cache per group
         Workload("fp8_36layers_groups4_b32_ctx2k_8k", B=32, Hq=32, Hkv=4, D=128,
                  block_size=16, max_blocks=512, kv_dtype="fp8",
@@ -270,6 +288,60 @@ def generate(wl: Workload, seed: Optional[int] = None,
     return PagedInputs(wl=wl, context_lens=ctx, block_tables=tables, num_blocks=num_blocks,
                        live=live, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
                        query=query, scale=np.float32(1.0 / math.sqrt(D)))
+
+
+@dataclass
+class MultiQueryInputs:
+    """Host arrays of a multi-query step (all numpy, C-contiguous)."""
+
+    base: PagedInputs                  # lengths, tables, pools (write slots poisoned)
+    query_lens: np.ndarray             # [B] int32, 0 <= q_b <= T_b
+    query_start: np.ndarray            # [B + 1] int32, prefix sums of query_lens
+    k_rows: List[np.ndarray]           # per group [rows, Hkv, D] bf16 bits
+    v_rows: List[np.ndarray]
+    query: np.ndarray                  # [layers, rows, Hq, D] bf16 bits
+
+    @property
+    def wl(self) -> Workload:
+        return self.base.wl
+
+    @property
+    def rows(self) -> int:
+        return int(self.query_start[-1])
+
+
+def generate_multiquery(wl: Workload, seed: Optional[int] = None,
+                        groups: Optional[List[int]] = None,
+                        query_lens: Optional[np.ndarray] = None) -> MultiQueryInputs:
+    """Draws a step in which sequence b writes and attends q_b new tokens.
+
+    query_lens overrides the drawn q_b (each clipped to [0, T_b])."""
+    seed = wl.seed if seed is None else int(seed)
+    base = generate(wl, seed, groups)
+    ctx = base.context_lens
+    if query_lens is None:
+        lo, hi = wl.q_uniform
+        rng = np.random.default_rng([seed, _S_QLEN])
+        q = rng.integers(lo, hi, size=wl.B, endpoint=True)
+    else:
+        q = np.asarray(query_lens, dtype=np.int64)
+    q = np.clip(q, 0, ctx).astype(np.int32)
+    qs = np.zeros(wl.B + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(q)
+    rows = int(qs[-1])
+    bs = wl.block_size
+    for pool in base.k_pool + base.v_pool:
+        for b in range(wl.B):
+            for t in range(int(ctx[b]) - int(q[b]), int(ctx[b])):
+                pool[int(base.block_tables[b, t // bs]), t % bs] = BF16_QNAN
+    groups = list(range(wl.groups)) if groups is None else list(groups)
+    n = rows * wl.Hkv * wl.D
+    k_rows = [_normal_bf16((seed, _S_KROWS, g), n).reshape(rows, wl.Hkv, wl.D) for g in groups]
+    v_rows = [_normal_bf16((seed, _S_VROWS, g), n).reshape(rows, wl.Hkv, wl.D) for g in groups]
+    query = _normal_bf16((seed, _S_QROWS), wl.layers * rows * wl.Hq * wl.D,
+                         sigma=1.0 / math.sqrt(wl.D)).reshape(wl.layers, rows, wl.Hq, wl.D)
+    return MultiQueryInputs(base=base, query_lens=q, query_start=qs, k_rows=k_rows,
+                            v_rows=v_rows, query=query)
 
 
 def random_partials(seed: int, context_lens: np.ndarray, Hq: int, D: int,

@@ -16,7 +16,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_formula.py", "tests/test_oracle_fp8.py",
-        "tests/test_oracle_attention.py"]
+        "tests/test_oracle_attention.py", "tests/test_oracle_multiquery.py"]
 
 # (name, original text, planted text, occurrence count expected)
 MUTANTS = [
@@ -55,6 +55,13 @@ MUTANTS = [
      "for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)"),
     ("split_range_overlaps", "int32_t t0 = s * split_tokens;",
      "int32_t t0 = s > 0 ? s * split_tokens - 1 : 0;"),
+    ("mq_position_off_by_one", "int32_t p = T - q + i;", "int32_t p = T - q + i - 1;"),
+    ("mq_not_causal", "kv_dtype, scale, 0, hq, 0, p + 1,", "kv_dtype, scale, 0, hq, 0, T,"),
+    ("mq_query_row_of_sequence", "const uint16_t* qrow = query + row * Hq * D;",
+     "const uint16_t* qrow = query + (int64_t)b * Hq * D;"),
+    ("write_rows_reversed", "int32_t t = T - q + i;", "int32_t t = T - 1 - i;"),
+    ("write_v_with_k_scale", "orc_e4m3_quantize(v_rows[src], v_scale[",
+     "orc_e4m3_quantize(v_rows[src], k_scale["),
 ]
 
 

@@ -103,3 +103,26 @@ def test_value_distribution():
     assert abs(k.mean()) < 0.01 and abs(k.std() - 1.0) < 0.01
     q = f32_from_bf16_bits(inp.query).astype(np.float64)
     assert abs(q.std() * np.sqrt(128) - 1.0) < 0.05
+
+
+def test_multiquery_layout_and_poison():
+    from synthetic import generate_multiquery
+
+    wl = WORKLOADS["tiny_mq_b4_hq8_hkv2_d64_bs16"]
+    mq = generate_multiquery(wl)
+    ctx = mq.base.context_lens
+    assert (mq.query_lens >= 0).all() and (mq.query_lens <= ctx).all()
+    assert mq.query_lens[0] == 1                      # clipped to T_0 = 1
+    assert mq.query_start[0] == 0 and np.array_equal(np.diff(mq.query_start), mq.query_lens)
+    assert mq.k_rows[0].shape == (mq.rows, wl.Hkv, wl.D)
+    assert mq.query.shape == (1, mq.rows, wl.Hq, wl.D)
+    for b in range(wl.B):
+        T, q = int(ctx[b]), int(mq.query_lens[b])
+        for t in range(T):
+            p = mq.base.block_tables[b, t // wl.block_size]
+            row = mq.base.k_pool[0][p, t % wl.block_size]
+            assert (row == 0x7FC0).all() == (t >= T - q), (b, t)
+    again = generate_multiquery(wl)
+    assert np.array_equal(again.query, mq.query) and np.array_equal(again.k_rows[0], mq.k_rows[0])
+    fixed = generate_multiquery(wl, query_lens=np.array([5, 5, 5, 5]))
+    assert list(fixed.query_lens) == [1, 5, 5, 5]
