@@ -232,6 +232,90 @@ int paged_decode_attention_balanced(const uint16_t* query,
 int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t block_size, int32_t kv_dtype);
 
+/*
+ * ---------------------------------------------------------------------
+ * Several new tokens per sequence in one step: a chunk of a long prompt
+ * ([B] "Continuous Batching": chunked prefill feeds a prompt in pieces
+ * interleaved with decodes) or the draft tokens a target model verifies
+ * in one pass ([A] "How does speculative decoding interact with KV-cache
+ * compression").  Sequence b brings q_b = query_start[b+1] -
+ * query_start[b] new tokens, its LAST q_b positions: row query_start[b] + i
+ * is position p = T_b - q_b + i, where T_b = context_lens[b] counts the new
+ * tokens.  Rows are laid out [total_rows, H, D] (H = Hkv for K/V rows, Hq
+ * for queries and outputs).
+ *
+ * Device-side preconditions (not checked by the kernels): query_start is
+ * non-decreasing with 0 <= q_b <= T_b and query_start[B] <= total_rows;
+ * the table covers ceil(T_b / block_size) blocks of each sequence.
+ * ---------------------------------------------------------------------
+ */
+
+/*
+ * paged_kv_write -- store each sequence's q_b new K/V rows at positions
+ * T_b - q_b .. T_b - 1 (the single-token append is q_b = 1).
+ *
+ *  k_rows, v_rows : [total_rows, Hkv, D] bf16 bits (device, 16-byte aligned).
+ *  query_start    : [B + 1] int32 row offsets (device).
+ *  max_query_len  : >= max_b q_b (host); sizes the launch, rows past q_b of
+ *                   a sequence are never read.
+ *  Other arguments, fp8 encoding and errors as paged_kv_append; B > 65535
+ *  or max_query_len > 2^25 is PKV_EUNSUPPORTED.  fp8 writes use the block's
+ *  existing scale and saturate to +-448.
+ */
+int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows,
+                   const int32_t* query_start,
+                   void* k_cache, void* v_cache,
+                   const float* k_scale, const float* v_scale,
+                   const int32_t* block_tables, int32_t max_blocks,
+                   const int32_t* context_lens,
+                   int32_t B, int32_t max_query_len, int32_t Hkv, int32_t D,
+                   int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                   void* stream);
+
+/*
+ * paged_multiquery_attention -- causal attention of every new token: row
+ * query_start[b] + i (position p = T_b - q_b + i) attends over tokens
+ * [0, p] of sequence b, query head hq through kv head hq / (Hq / Hkv), with
+ * the same scaled softmax as paged_decode_attention.  Call after
+ * paged_kv_write of the same rows.  Scheduled like
+ * paged_decode_attention_balanced: every sequence's tokens are streamed
+ * once per kv head while its q_b * G (new row, query head) pairs are at
+ * most 32, once per 32 pairs beyond that.
+ *
+ *  query          : [total_rows, Hq, D] bf16 bits (device, 16-byte aligned).
+ *  query_start    : [B + 1] int32 (device); total_rows, max_query_len host.
+ *  workspace      : device scratch of >= workspace_bytes, 16-byte aligned,
+ *                   caller-owned, contents on entry irrelevant; calls that
+ *                   share one must be ordered on one stream.
+ *  workspace_bytes: >= paged_multiquery_workspace_size(Hq, Hkv, D,
+ *                   block_size, kv_dtype, max_query_len).
+ *  out            : [total_rows, Hq, D] float; lse_out [total_rows, Hq]
+ *                   float (natural log) or NULL.  Rows of no sequence are
+ *                   untouched.
+ *  Returns PKV_EINVAL for bad arguments or a small workspace,
+ *  PKV_EUNSUPPORTED for shapes outside the kernel set (as the decode) or
+ *  more than 2^25 tokens per sequence.
+ */
+int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start,
+                               int32_t total_rows, int32_t max_query_len,
+                               const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks,
+                               const int32_t* context_lens,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t kv_dtype, float scale,
+                               void* workspace, int64_t workspace_bytes,
+                               float* out, float* lse_out, void* stream);
+
+/*
+ * Bytes of workspace paged_multiquery_attention needs on the current
+ * device for these shapes and max_query_len, or a negative pkv_status.
+ */
+int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t block_size, int32_t kv_dtype,
+                                        int32_t max_query_len);
+
 /* Human-readable name of a pkv_status value (static storage). */
 const char* pkv_status_string(int status);
 

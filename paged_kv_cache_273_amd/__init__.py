@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
     paged_decode_attention(...)   attention of one query per sequence over
                                   its block-table-gathered cache
     split_context_reduce(...)     log-sum-exp merge of split-context partials
+    paged_decode_attention_balanced(...)  the decode attention, work-balanced
+    paged_kv_write(...)           several new K/V rows per sequence
+    paged_multiquery_attention(...)  causal attention of several new tokens
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ PKV_BF16, PKV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "paged_decode_attention_balanced", "paged_decode_workspace_size",
+           "paged_kv_write", "paged_multiquery_attention", "paged_multiquery_workspace_size",
            "pkv_status_string")
 
 
@@ -55,6 +59,13 @@ def _load(path=LIB_PATH):
                                                   C.c_float, P, C.c_int64, P, P, P]
     L.paged_decode_workspace_size.restype = C.c_int64
     L.paged_decode_workspace_size.argtypes = [I, I, I, I, I]
+    L.paged_kv_write.restype = C.c_int
+    L.paged_kv_write.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, P]
+    L.paged_multiquery_attention.restype = C.c_int
+    L.paged_multiquery_attention.argtypes = [P, P, I, I, P, P, P, P, P, I, P, I, I, I, I, I, I,
+                                             I, C.c_float, P, C.c_int64, P, P, P]
+    L.paged_multiquery_workspace_size.restype = C.c_int64
+    L.paged_multiquery_workspace_size.argtypes = [I, I, I, I, I, I]
     L.pkv_status_string.restype = C.c_char_p
     L.pkv_status_string.argtypes = [C.c_int]
     return L
@@ -209,6 +220,76 @@ def split_context_reduce(partial_out, partial_lse, context_lens, split_tokens, *
                                    Hq, D, int(split_tokens), ms, _ptr(out), _ptr(lse_out),
                                    _stream(stream))
     _check("split_context_reduce", st)
+    return out
+
+
+def paged_kv_write(k_rows, v_rows, query_start, k_cache, v_cache, block_tables, context_lens,
+                   max_query_len, *, k_scale=None, v_scale=None, stream=None) -> None:
+    """k_rows/v_rows [rows, Hkv, D] bf16: rows query_start[b] + i go to
+    positions context_lens[b] - q_b + i (q_b = query_start[b+1] -
+    query_start[b] <= max_query_len)."""
+    _need(k_rows, _BF16_BITS, "k_rows")
+    _need(v_rows, _BF16_BITS, "v_rows")
+    _need(query_start, (torch.int32,), "query_start")
+    _need(block_tables, (torch.int32,), "block_tables")
+    _need(context_lens, (torch.int32,), "context_lens")
+    _, Hkv, D = k_rows.shape
+    B = context_lens.shape[0]
+    if query_start.shape[0] != B + 1:
+        raise ValueError("query_start must hold B + 1 offsets")
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    st = _lib.paged_kv_write(_ptr(k_rows), _ptr(v_rows), _ptr(query_start), _ptr(k_cache),
+                             _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                             block_tables.shape[1], _ptr(context_lens), B, int(max_query_len),
+                             Hkv, D, bs, nb, _kv_dtype(k_cache), _stream(stream))
+    _check("paged_kv_write", st)
+
+
+def paged_multiquery_workspace_size(Hq, Hkv, D, block_size, max_query_len,
+                                    kv_dtype=PKV_BF16) -> int:
+    """Bytes of workspace paged_multiquery_attention needs on the current
+    device."""
+    n = int(_lib.paged_multiquery_workspace_size(Hq, Hkv, D, block_size, kv_dtype,
+                                                 int(max_query_len)))
+    if n < 0:
+        _check("paged_multiquery_workspace_size", n)
+    return n
+
+
+def make_multiquery_workspace(query, k_cache, max_query_len) -> torch.Tensor:
+    """A device buffer large enough for paged_multiquery_attention."""
+    _, Hq, D = query.shape
+    n = paged_multiquery_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
+                                        max_query_len, _kv_dtype(k_cache))
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_tables, context_lens,
+                               scale, max_query_len, *, workspace, out=None, lse_out=None,
+                               k_scale=None, v_scale=None, stream=None):
+    """query [rows, Hq, D] bf16: row query_start[b] + i (position
+    context_lens[b] - q_b + i) attends causally over its sequence's tokens
+    up to its own position.  Writes out [rows, Hq, D] float32 (and lse_out
+    [rows, Hq]) and returns out."""
+    _need(query, _BF16_BITS, "query")
+    _need(query_start, (torch.int32,), "query_start")
+    _need(block_tables, (torch.int32,), "block_tables")
+    _need(context_lens, (torch.int32,), "context_lens")
+    rows, Hq, D = query.shape
+    B = context_lens.shape[0]
+    if query_start.shape[0] != B + 1:
+        raise ValueError("query_start must hold B + 1 offsets")
+    nb, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty((rows, Hq, D), dtype=torch.float32, device=query.device)
+    _need(out, (torch.float32,), "out")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.paged_multiquery_attention(
+        _ptr(query), _ptr(query_start), rows, int(max_query_len), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, Hq, Hkv, D, bs, nb, _kv_dtype(k_cache), float(scale),
+        _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out), _stream(stream))
+    _check("paged_multiquery_attention", st)
     return out
 
 

@@ -153,6 +153,8 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     a.lse_out = lse_out;
     a.partial_out = partial_out;
     a.partial_lse = partial_lse;
+    a.query_start = nullptr;
+    a.total_rows = 0;
     a.max_blocks = max_blocks;
     a.B = B;
     a.Hq = Hq;
@@ -246,6 +248,8 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     a.lse_out = lse_out;
     a.partial_out = nullptr;
     a.partial_lse = nullptr;
+    a.query_start = nullptr;
+    a.total_rows = 0;
     a.max_blocks = max_blocks;
     a.B = B;
     a.Hq = Hq;
@@ -268,6 +272,173 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
     return launched(pkv::launch_decode_balanced(a, ws, D, block_size, kv_dtype, nt,
                                                 (hipStream_t)stream));
+}
+
+int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows, const int32_t* query_start,
+                   void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                   const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                   int32_t B, int32_t max_query_len, int32_t Hkv, int32_t D, int32_t block_size,
+                   int32_t num_blocks, int32_t kv_dtype, void* stream)
+{
+    if (B < 0 || max_query_len < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0
+        || max_blocks <= 0)
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size))
+        return PKV_EUNSUPPORTED;
+    if (B > 65535 || (int64_t)max_query_len > kMaxTokens)
+        return PKV_EUNSUPPORTED;
+    if (B == 0 || max_query_len == 0)
+        return PKV_OK;
+    if (!k_rows || !v_rows || !query_start || !k_cache || !v_cache || !block_tables
+        || !context_lens)
+        return PKV_EINVAL;
+    const uintptr_t cache_align = kv_dtype == PKV_FP8_E4M3 ? 8 : 16;
+    if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(k_cache, cache_align)
+        || !aligned(v_cache, cache_align))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    pkv::WriteArgs a;
+    a.k_rows = k_rows;
+    a.v_rows = v_rows;
+    a.query_start = query_start;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks = max_blocks;
+    a.B = B;
+    a.max_query_len = max_query_len;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.block_size = block_size;
+    a.kv_dtype = kv_dtype;
+    return launched(pkv::launch_write(a, (hipStream_t)stream));
+}
+
+// 16-column MFMA tiles per wave of the multi-query kernel: two once a kv
+// head has more than 16 (new row, query head) columns.
+static int mq_tiles_per_wave(int32_t max_query_len, int32_t G)
+{
+    return (int64_t)max_query_len * G > 16 ? 2 : 1;
+}
+
+static int mq_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype, int nct)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int hg = pkv::balanced_head_group(Hkv);
+    return cus * pkv::multiquery_groups_per_cu(D, block_size, kv_dtype, hg, nct);
+}
+
+static int64_t mq_bytes(int ngroups, int32_t Hkv, int nct, int32_t D)
+{
+    const int64_t rows = (int64_t)2 * ngroups * pkv::balanced_head_group(Hkv) * 16 * nct;
+    return rows * (D + 1) * (int64_t)sizeof(float);
+}
+
+int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                        int32_t kv_dtype, int32_t max_query_len)
+{
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_query_len < 0)
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup
+        || (int64_t)max_query_len > kMaxTokens)
+        return PKV_EUNSUPPORTED;
+    const int nct = mq_tiles_per_wave(max_query_len, Hq / Hkv);
+    const int n = mq_groups(Hkv, D, block_size, kv_dtype, nct);
+    if (n <= 0)
+        return PKV_ELAUNCH;
+    return mq_bytes(n, Hkv, nct, D);
+}
+
+int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start,
+                               int32_t total_rows, int32_t max_query_len, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks,
+                               const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t block_size, int32_t num_blocks,
+                               int32_t kv_dtype, float scale, void* workspace,
+                               int64_t workspace_bytes, float* out, float* lse_out,
+                               void* stream)
+{
+    if (B < 0 || total_rows < 0 || max_query_len < 0 || Hq <= 0 || Hkv <= 0 || D <= 0
+        || block_size <= 0 || num_blocks <= 0 || max_blocks <= 0 || workspace_bytes < 0)
+        return PKV_EINVAL;
+    if (Hq % Hkv != 0 || !isfinite(scale))
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
+        return PKV_EUNSUPPORTED;
+    if ((int64_t)max_blocks * block_size > kMaxTokens || (int64_t)max_query_len > kMaxTokens)
+        return PKV_EUNSUPPORTED;
+    if (B == 0 || total_rows == 0)
+        return PKV_OK;
+    if (max_query_len == 0)
+        return PKV_EINVAL;                       // rows to attend but no new tokens
+    if (!query || !query_start || !k_cache || !v_cache || !block_tables || !context_lens || !out
+        || !workspace)
+        return PKV_EINVAL;
+    if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)
+        || !aligned(out, 16) || !aligned(workspace, 16) || (lse_out && !aligned(lse_out, 4)))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    const int32_t G = Hq / Hkv;
+    const int nct = mq_tiles_per_wave(max_query_len, G);
+    const int n = mq_groups(Hkv, D, block_size, kv_dtype, nct);
+    if (n <= 0)
+        return PKV_ELAUNCH;
+    if (workspace_bytes < mq_bytes(n, Hkv, nct, D))
+        return PKV_EINVAL;
+    pkv::DecodeArgs a;
+    a.query = query;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse_out = lse_out;
+    a.partial_out = nullptr;
+    a.partial_lse = nullptr;
+    a.query_start = query_start;
+    a.total_rows = total_rows;
+    a.max_blocks = max_blocks;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.split_tokens = 0;
+    a.max_splits = 1;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    pkv::BalanceArgs ws;
+    ws.head_group = pkv::balanced_head_group(Hkv);
+    ws.ngroups_launched = n;
+    ws.part_out = (float*)workspace;
+    ws.part_lse = ws.part_out + (size_t)2 * n * ws.head_group * 16 * nct * D;
+    // range boundaries in double precision: (tiles of the call) * (groups
+    // launched) must stay below 2^52
+    const int64_t ngroups = Hkv / ws.head_group;
+    const int64_t col_groups = ((int64_t)max_query_len * G + 16 * nct - 1) / (16 * nct);
+    const int64_t max_tiles =
+        (int64_t)B * (((int64_t)max_blocks * block_size + 31) / 32) * col_groups * ngroups;
+    if (max_tiles * ((int64_t)n + 1) >= ((int64_t)1 << 52))
+        return PKV_EUNSUPPORTED;
+    const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
+    return launched(pkv::launch_multiquery(a, ws, D, block_size, kv_dtype, nct, nt,
+                                           (hipStream_t)stream));
 }
 
 int split_context_reduce(const float* partial_out, const float* partial_lse,

@@ -1,5 +1,6 @@
-// append_reduce.hip -- the two small kernels around paged decode attention:
+// append_reduce.hip -- the small kernels around paged decode attention:
 //   * paged_kv_append: scatter the step's new K/V rows into their slots;
+//   * paged_kv_write: the same for several new tokens per sequence;
 //   * split_context_reduce: log-sum-exp merge of split-context partials.
 //
 // Pages cited:
@@ -19,6 +20,34 @@ namespace {
 // One thread moves 8 elements (16 bytes of bf16 input) of one (b, h) row.
 // fp8 ([B] "FP8 KV cache"): code = E4M3FN(float(x) / scale[p, h]) with a
 // correctly rounded binary32 division.
+// Moves 8 elements (16 bytes of bf16 input) of one K row and one V row
+// into the cache at element offset dst (block scales ks / vs for fp8).
+template <int FP8>
+__device__ __forceinline__ void store8(const uint16_t* k_src, const uint16_t* v_src,
+                                       void* k_cache, void* v_cache, size_t dst, float ks,
+                                       float vs)
+{
+    const u32x4 kx = *(const u32x4*)k_src;
+    const u32x4 vx = *(const u32x4*)v_src;
+    if (!FP8) {
+        *(u32x4*)((uint16_t*)k_cache + dst) = kx;
+        *(u32x4*)((uint16_t*)v_cache + dst) = vx;
+        return;
+    }
+    u32x2 kq = {0u, 0u}, vq = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t kb = (kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t vb = (vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t kc = f32_to_e4m3_sat(bf16_bits_to_f32(kb) / ks);
+        const uint32_t vc = f32_to_e4m3_sat(bf16_bits_to_f32(vb) / vs);
+        kq[i / 4] |= kc << (8 * (i & 3));
+        vq[i / 4] |= vc << (8 * (i & 3));
+    }
+    *(u32x2*)((uint8_t*)k_cache + dst) = kq;
+    *(u32x2*)((uint8_t*)v_cache + dst) = vq;
+}
+
 template <int FP8>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 {
@@ -38,27 +67,45 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     const int slot = t % a.block_size;
     const size_t src = ((size_t)b * a.Hkv + h) * a.D + 8 * c;
     const size_t dst = (((size_t)p * a.block_size + slot) * a.Hkv + h) * a.D + 8 * c;
-    const u32x4 kx = *(const u32x4*)(a.k_new + src);
-    const u32x4 vx = *(const u32x4*)(a.v_new + src);
-    if (!FP8) {
-        *(u32x4*)((uint16_t*)a.k_cache + dst) = kx;
-        *(u32x4*)((uint16_t*)a.v_cache + dst) = vx;
+    float ks = 1.f, vs = 1.f;
+    if (FP8) {
+        ks = a.k_scale[(size_t)p * a.Hkv + h];
+        vs = a.v_scale[(size_t)p * a.Hkv + h];
+    }
+    store8<FP8>(a.k_new + src, a.v_new + src, a.k_cache, a.v_cache, dst, ks, vs);
+}
+
+// ---------------------------------------------------------------- write
+// Several new tokens per sequence (a prefill chunk, [B] "Continuous
+// Batching"; draft tokens under verification): row query_start[b] + i goes
+// to position T_b - q_b + i.  Grid (x: rows i x heads x 8-element chunks
+// up to max_query_len rows, y: sequence b); threads past q_b exit.
+template <int FP8>
+__global__ __launch_bounds__(256) void write_kernel(WriteArgs a)
+{
+    const int per_row = a.D / 8;
+    const int b = blockIdx.y;
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int row0 = a.query_start[b];
+    const int q = a.query_start[b + 1] - row0;
+    if (gid >= (long long)q * a.Hkv * per_row)
         return;
+    const int c = (int)(gid % per_row);
+    const int h = (int)((gid / per_row) % a.Hkv);
+    const int i = (int)(gid / ((long long)per_row * a.Hkv));
+    const int t = a.context_lens[b] - q + i;
+    if (t < 0)
+        return;                                  // more new rows than tokens
+    const int p = a.block_tables[(size_t)b * a.max_blocks + t / a.block_size];
+    const int slot = t % a.block_size;
+    const size_t src = ((size_t)(row0 + i) * a.Hkv + h) * a.D + 8 * c;
+    const size_t dst = (((size_t)p * a.block_size + slot) * a.Hkv + h) * a.D + 8 * c;
+    float ks = 1.f, vs = 1.f;
+    if (FP8) {
+        ks = a.k_scale[(size_t)p * a.Hkv + h];
+        vs = a.v_scale[(size_t)p * a.Hkv + h];
     }
-    const float ks = a.k_scale[(size_t)p * a.Hkv + h];
-    const float vs = a.v_scale[(size_t)p * a.Hkv + h];
-    u32x2 kq = {0u, 0u}, vq = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t kb = (kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t vb = (vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t kc = f32_to_e4m3_sat(bf16_bits_to_f32(kb) / ks);
-        const uint32_t vc = f32_to_e4m3_sat(bf16_bits_to_f32(vb) / vs);
-        kq[i / 4] |= kc << (8 * (i & 3));
-        vq[i / 4] |= vc << (8 * (i & 3));
-    }
-    *(u32x2*)((uint8_t*)a.k_cache + dst) = kq;
-    *(u32x2*)((uint8_t*)a.v_cache + dst) = vq;
+    store8<FP8>(a.k_rows + src, a.v_rows + src, a.k_cache, a.v_cache, dst, ks, vs);
 }
 
 // ---------------------------------------------------------------- reduce
@@ -168,6 +215,22 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream)
         hipLaunchKernelGGL(append_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(append_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream)
+{
+    const long long per_seq = (long long)a.max_query_len * a.Hkv * (a.D / 8);
+    if (per_seq <= 0 || a.B <= 0)
+        return hipSuccess;
+    const long long blocks = (per_seq + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL || a.B > 65535)
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks, (unsigned)a.B);
+    if (a.kv_dtype == 1)
+        hipLaunchKernelGGL(write_kernel<1>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(write_kernel<0>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

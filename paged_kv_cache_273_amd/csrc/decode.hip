@@ -88,8 +88,19 @@ struct Cfg {
     static constexpr int DT = D / 16;                   // 16-wide d tiles of the output
     static constexpr int PITCH = D * 2 + 8;             // LDS row pitch (bf16 rows), bytes
     static constexpr int LDS_BYTES = kTile * PITCH;     // per wave
+    static constexpr int Q_BYTES = KSTEPS * kWave * 16;  // Q operands of one column tile
     static_assert(16 % V_RPI == 0, "a V load must stay inside one 16-token block");
 };
+
+// LDS slice of one wave: the V staging tile, plus the Q operands when a
+// wave has several column tiles (their registers would not fit beside the
+// accumulators and the tile in flight; each lane reads back only what it
+// wrote, so the slice needs no barrier).
+template <int D, int FP8, int NCT>
+constexpr int wave_lds_bytes()
+{
+    return Cfg<D, FP8>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, FP8>::Q_BYTES : 0);
+}
 
 // First of the 8 consecutive head-dim elements that lane group q feeds to
 // MFMA k-step j.  bf16: one 16-byte load per k-step (chunk q + 4j of
@@ -130,33 +141,69 @@ struct RangeAcc {
     float l;
 };
 
-// One wave attends the G query heads of kv head h of sequence b over the
-// logical tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.
-template <int D, int BS, int FP8, int NT>
+// The MFMA columns of one wave: NCT tiles of 16 columns, each column one
+// (query row, query head) pair that reads the wave's kv head.  A decode
+// step has one tile whose columns are the G heads of the group; several
+// new tokens per sequence give each column its own row and causal limit.
+template <int NCT>
+struct Cols {
+    const uint16_t* qrow[NCT];   // this lane's query vector per column tile
+    bool live[NCT];              // the column is a real (row, head) pair
+    int lim[NCT];                // causal limit: tokens t < lim are visible
+    int mask_from;               // uniform: no column's limit lies below it
+};
+
+// Decode columns: column r16 is query head h * G + r16 of sequence b.
+__device__ __forceinline__ Cols<1> decode_cols(const DecodeArgs& a, int b, int h, int D)
+{
+    const int r16 = __lane_id() & 15;
+    Cols<1> cs;
+    cs.live[0] = r16 < a.G;
+    cs.qrow[0] = a.query + ((size_t)b * a.Hq + (cs.live[0] ? h * a.G + r16 : 0)) * D;
+    cs.lim[0] = 0x7FFFFFFF;
+    cs.mask_from = 0x7FFFFFFF;
+    return cs;
+}
+
+// One wave attends its columns (kv head h of sequence b) over the logical
+// tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.  With
+// CAUSAL, tokens at or past a column's limit are masked as well; a column
+// that sees no token of the range ends with l = 0.
+template <int D, int BS, int FP8, int NT, int NCT, bool CAUSAL>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
-                                             int h, int t_begin, int t_end, RangeAcc<D>& r)
+                                             int h, int t_begin, int t_end,
+                                             const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT])
 {
     using C = Cfg<D, FP8>;
     const int lane = __lane_id();
     const int q4 = lane >> 4;
     const int r16 = lane & 15;
     const int Hkv = a.Hkv;
-    const int G = a.G;
-    const int hq = h * G + r16;
-    const bool live_col = r16 < G;
 
-    // Q^T operand: column r16 = query head h*G + r16 (zero past G).
-    bf16x8 qf[C::KSTEPS];
-    {
-        const uint16_t* qrow = a.query + ((size_t)b * a.Hq + (live_col ? hq : 0)) * D;
+    // Q^T operands: column r16 of tile j is this lane's query (zero if
+    // dead); in registers for one column tile, in LDS for several.
+    constexpr bool QLDS = NCT > 1;
+    volatile u32x4* qlds = (volatile u32x4*)(lds + C::LDS_BYTES);
+    bf16x8 qf[QLDS ? 1 : NCT][C::KSTEPS];
 #pragma unroll
-        for (int j = 0; j < C::KSTEPS; ++j) {
-            u32x4 v = *(const u32x4*)(qrow + kdim_base<FP8>(j, q4));
-            if (!live_col)
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int k = 0; k < C::KSTEPS; ++k) {
+            u32x4 v = *(const u32x4*)(cs.qrow[j] + kdim_base<FP8>(k, q4));
+            if (!cs.live[j])
                 v = u32x4{0u, 0u, 0u, 0u};
-            qf[j] = as_bf16x8(v);
+            if (QLDS)
+                qlds[(j * C::KSTEPS + k) * kWave + lane] = v;
+            else
+                qf[QLDS ? 0 : j][k] = as_bf16x8(v);
         }
-    }
+    auto qop = [&](int j, int k) -> bf16x8 {
+        if (QLDS) {
+            const u32x4 v = qlds[(j * C::KSTEPS + k) * kWave + lane];
+            return as_bf16x8(v);
+        }
+        return qf[QLDS ? 0 : j][k];
+    };
 
     // Block-table window of this unit, 64 entries per VGPR load.
     const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
@@ -190,8 +237,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     uint32_t v_off[C::V_LOADS];
 #pragma unroll
     for (int k = 0; k < C::V_LOADS; ++k) {
-        const int r = k * C::V_RPI + lane / C::V_LPR;
-        v_off[k] = (uint32_t)(BS == 16 ? (r & 15) : r) * tok_stride + head_off
+        const int rr = k * C::V_RPI + lane / C::V_LPR;
+        v_off[k] = (uint32_t)(BS == 16 ? (rr & 15) : rr) * tok_stride + head_off
                    + 16 * (lane % C::V_LPR);
     }
 
@@ -231,112 +278,131 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         }
     };
 
-    f32x4 (&acc)[C::DT] = r.acc;
-    float& m_run = r.m;
-    float& l_run = r.l;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-        acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run = -__builtin_inff();
-    l_run = 0.f;
+    for (int j = 0; j < NCT; ++j) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+            r[j].acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        r[j].m = -__builtin_inff();
+        r[j].l = 0.f;
+    }
     const float sl2 = a.scale_log2;
 
     // V rows -> LDS as bf16 (zeroed past the range end).
     auto stage_v = [&](int t0, const Tile<D, FP8>& tl, bool masked) {
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
-            const int r = k * C::V_RPI + lane / C::V_LPR;
+            const int rr = k * C::V_RPI + lane / C::V_LPR;
             const int c = lane % C::V_LPR;
             u32x4 v = tl.v[k];
-            if (masked && t0 + r >= t_end)
+            if (masked && t0 + rr >= t_end)
                 v = u32x4{0u, 0u, 0u, 0u};
             if (FP8) {
                 u32x4 lo, hi;
                 fp8x16_to_bf16x16(v, lo, hi);
-                u32x2* dst = (u32x2*)(lds + r * C::PITCH + 32 * c);
+                u32x2* dst = (u32x2*)(lds + rr * C::PITCH + 32 * c);
                 dst[0] = u32x2{lo[0], lo[1]};
                 dst[1] = u32x2{lo[2], lo[3]};
                 dst[2] = u32x2{hi[0], hi[1]};
                 dst[3] = u32x2{hi[2], hi[3]};
             } else {
-                u32x2* dst = (u32x2*)(lds + r * C::PITCH + 16 * c);
+                u32x2* dst = (u32x2*)(lds + rr * C::PITCH + 16 * c);
                 dst[0] = u32x2{v[0], v[1]};
                 dst[1] = u32x2{v[2], v[3]};
             }
         }
     };
 
-    // scores S^T[token][head] of the two 16-token halves
-    auto qk = [&](const Tile<D, FP8>& tl, f32x4 (&sacc)[2]) {
+    // scores S^T[token][column] of the two 16-token halves, every column
+    // tile sharing each K operand
+    auto qk = [&](const Tile<D, FP8>& tl, f32x4 (&sacc)[NCT][2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NCT; ++j)
+                sacc[j][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < C::K_LOADS; ++c) {
                 if (FP8) {
                     u32x4 lo, hi;
                     fp8x16_to_bf16x16(tl.k[tau][c], lo, hi);
-                    sacc[tau] = mfma_16x16x32(as_bf16x8(lo), qf[2 * c], sacc[tau]);
-                    sacc[tau] = mfma_16x16x32(as_bf16x8(hi), qf[2 * c + 1], sacc[tau]);
+#pragma unroll
+                    for (int j = 0; j < NCT; ++j) {
+                        sacc[j][tau] = mfma_16x16x32(as_bf16x8(lo), qop(j, 2 * c), sacc[j][tau]);
+                        sacc[j][tau] =
+                            mfma_16x16x32(as_bf16x8(hi), qop(j, 2 * c + 1), sacc[j][tau]);
+                    }
                 } else {
-                    sacc[tau] = mfma_16x16x32(as_bf16x8(tl.k[tau][c]), qf[c], sacc[tau]);
+#pragma unroll
+                    for (int j = 0; j < NCT; ++j)
+                        sacc[j][tau] = mfma_16x16x32(as_bf16x8(tl.k[tau][c]), qop(j, c),
+                                                     sacc[j][tau]);
                 }
             }
         }
     };
 
     // online softmax update and O^T += V^T . P^T from the staged V rows
-    auto softmax_pv = [&](int t0, const TileAddr& ta, const f32x4 (&sacc)[2], bool masked) {
-        float s[8];
+    auto softmax_pv = [&](int t0, const TileAddr& ta, const f32x4 (&sacc)[NCT][2],
+                          bool masked) {
+        bf16x8 pb[NCT], pb_lo[NCT];
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            const float f = FP8 ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
+        for (int j = 0; j < NCT; ++j) {
+            const int lim = CAUSAL ? min(t_end, cs.lim[j]) : t_end;
+            float s[8];
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const float f = FP8 ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = sacc[j][tau][i] * f;
+                    if (masked && t0 + 16 * tau + 4 * q4 + i >= lim)
+                        x = -__builtin_inff();
+                    s[4 * tau + i] = x;
+                }
+            }
+            float mt = s[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                mt = fmaxf(mt, s[i]);
+            mt = fmaxf(mt, xor_shuffle(mt, 16));
+            mt = fmaxf(mt, xor_shuffle(mt, 32));
+            const float m_new = fmaxf(r[j].m, mt);
+            // a column with nothing visible yet keeps m = -inf; its
+            // exponentials are then taken against 0 and all vanish
+            const float m_ref = (CAUSAL && m_new == -__builtin_inff()) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(r[j].m - m_ref);
+            r[j].m = m_new;
+            float p[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+                psum += p[i];
+            }
+            r[j].l = r[j].l * alpha + psum;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                r[j].acc[dt] *= alpha;
+            if (FP8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] *= ta.vsA;
+                    p[4 + i] *= ta.vsB;
+                }
+            }
+            // P as a two-term bf16 split, p = hi + lo (about 16 significant
+            // bits): one bf16 term alone loses too much when V terms cancel.
+            u32x4 pw, pr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x = sacc[tau][i] * f;
-                if (masked && t0 + 16 * tau + 4 * q4 + i >= t_end)
-                    x = -__builtin_inff();
-                s[4 * tau + i] = x;
+                pw[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+                pr[i] = pack_bf16x2(p[2 * i] - bf16_bits_to_f32(pw[i] & 0xFFFFu),
+                                    p[2 * i + 1] - bf16_bits_to_f32(pw[i] >> 16));
             }
+            pb[j] = as_bf16x8(pw);
+            pb_lo[j] = as_bf16x8(pr);
         }
-        float mt = s[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i)
-            mt = fmaxf(mt, s[i]);
-        mt = fmaxf(mt, xor_shuffle(mt, 16));
-        mt = fmaxf(mt, xor_shuffle(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float p[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-            psum += p[i];
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-            acc[dt] *= alpha;
-        if (FP8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] *= ta.vsA;
-                p[4 + i] *= ta.vsB;
-            }
-        }
-        // P as a two-term bf16 split, p = hi + lo (about 16 significant
-        // bits): one bf16 term alone loses too much when V terms cancel.
-        u32x4 pw, pr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pw[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-            pr[i] = pack_bf16x2(p[2 * i] - bf16_bits_to_f32(pw[i] & 0xFFFFu),
-                                p[2 * i + 1] - bf16_bits_to_f32(pw[i] >> 16));
-        }
-        const bf16x8 pb = as_bf16x8(pw);
-        const bf16x8 pb_lo = as_bf16x8(pr);
 
         const unsigned short* l16 = (const unsigned short*)lds;
 #pragma unroll
@@ -348,39 +414,50 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                 uint32_t hi = l16[(pv_token(q4, i + 1) * C::PITCH) / 2 + 16 * dt + r16];
                 vw[i / 2] = lo | (hi << 16);
             }
-            acc[dt] = mfma_16x16x32(as_bf16x8(vw), pb, acc[dt]);
-            acc[dt] = mfma_16x16x32(as_bf16x8(vw), pb_lo, acc[dt]);
+#pragma unroll
+            for (int j = 0; j < NCT; ++j) {
+                r[j].acc[dt] = mfma_16x16x32(as_bf16x8(vw), pb[j], r[j].acc[dt]);
+                r[j].acc[dt] = mfma_16x16x32(as_bf16x8(vw), pb_lo[j], r[j].acc[dt]);
+            }
         }
     };
 
     // One register set per wave: a tile's V registers are refilled with
     // the next tile as soon as they are staged in LDS, its K registers as
     // soon as the scores are formed; the next tile's 16 KB then stream in
-    // while this tile's softmax and PV product run.
+    // while this tile's softmax and PV product run.  Tiles that end at or
+    // before every column's limit skip the causal mask.
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+    int n_plain = ntiles - 1;
+    if (CAUSAL)
+        n_plain = max(0, min(n_plain, (min(t_end, cs.mask_from) - t_begin) / kTile));
     Tile<D, FP8> tl;
     TileAddr ta = tile_addr(t_begin);
     load_k(ta, tl);
     load_v(ta, tl);
-    for (int it = 0; it < ntiles - 1; ++it) {
+    auto step = [&](int it, bool masked) {
         const int t0 = t_begin + kTile * it;
         const TileAddr tn = tile_addr(t0 + kTile);
         stage_v(t0, tl, false);
         load_v(tn, tl);
-        f32x4 sacc[2];
+        f32x4 sacc[NCT][2];
         qk(tl, sacc);
         load_k(tn, tl);
-        softmax_pv(t0, ta, sacc, false);
+        softmax_pv(t0, ta, sacc, masked);
         ta = tn;
-    }
+    };
+    for (int it = 0; it < n_plain; ++it)
+        step(it, false);
+    if (CAUSAL)
+        for (int it = n_plain; it < ntiles - 1; ++it)
+            step(it, true);
     {
         const int t0 = t_begin + kTile * (ntiles - 1);
         stage_v(t0, tl, true);
-        f32x4 sacc[2];
+        f32x4 sacc[NCT][2];
         qk(tl, sacc);
         softmax_pv(t0, ta, sacc, true);
     }
-
 }
 
 // Sums the per-lane normalisers of each head column; returns 1/l and the
@@ -391,7 +468,7 @@ __device__ __forceinline__ void finish_range(const RangeAcc<D>& r, float& inv, f
     float l = r.l;
     l += xor_shuffle(l, 16);
     l += xor_shuffle(l, 32);
-    inv = 1.0f / l;
+    inv = l > 0.f ? 1.0f / l : 0.f;          // l = 0: nothing visible, output 0
     lse = (r.m + __builtin_log2f(l)) * kLn2;
 }
 
@@ -455,19 +532,20 @@ void decode_kernel(DecodeArgs a)
         }
         return;
     }
-    RangeAcc<D> r;
-    attend_range<D, BS, FP8, NT>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin, t_end, r);
+    RangeAcc<D> r[1];
+    attend_range<D, BS, FP8, NT, 1, false>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin,
+                                           t_end, decode_cols(a, b, h, D), r);
     float inv, lse;
-    finish_range<D>(r, inv, lse);
+    finish_range<D>(r[0], inv, lse);
     if (!live_col)
         return;
     if (SPLIT) {
         const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
-        store_row<D>(a.partial_out + row * D, r, inv);
+        store_row<D>(a.partial_out + row * D, r[0], inv);
         if (q4 == 0)
             a.partial_lse[row] = lse;
     } else {
-        store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r, inv);
+        store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r[0], inv);
         if (a.lse_out && q4 == 0)
             a.lse_out[(size_t)b * a.Hq + hq] = lse;
     }
@@ -487,6 +565,12 @@ void decode_kernel(DecodeArgs a)
 // normalised partial per piece in the workspace (slot 2r for a group's
 // first piece, 2r+1 for its last) and balanced_merge_kernel combines them
 // with the log-sum-exp rule.
+//
+// Several new tokens per sequence (MQ): the columns of kv head h are the
+// pairs (new row i, head g) in the order c = i * G + g, cut into column
+// groups of 16 * NCT; a unit is (sequence, head group, column group) and
+// covers the whole context, the causal limits masking what each column
+// may not see.
 
 constexpr int kMaxHeadGroup = 8;
 
@@ -495,39 +579,65 @@ __device__ __forceinline__ int tiles_of(int T)
     return (T + kTile - 1) / kTile;
 }
 
-// sum over sequences [0, b_end) of tiles_of(T_b) (same value in every lane)
-__device__ __forceinline__ long long tiles_before(const int32_t* ctx, int b_end)
+// Column groups of sequence b per head group: 1 for a decode step,
+// ceil(q_b * G / (16 * NCT)) for q_b new tokens.
+template <bool MQ, int NCT>
+__device__ __forceinline__ int col_groups(const DecodeArgs& a, int b)
+{
+    if (!MQ)
+        return 1;
+    const int q = a.query_start[b + 1] - a.query_start[b];
+    return (q * a.G + 16 * NCT - 1) / (16 * NCT);
+}
+
+// Tiles of all units of sequence b of one head group.
+template <bool MQ, int NCT>
+__device__ __forceinline__ long long seq_tiles(const DecodeArgs& a, int b)
+{
+    return (long long)tiles_of(a.context_lens[b]) * col_groups<MQ, NCT>(a, b);
+}
+
+template <bool MQ>
+__device__ __forceinline__ long long wave_sum_w(long long v)
+{
+    return MQ ? wave_sum_ll(v) : (long long)wave_sum_i((int)v);
+}
+
+// sum over sequences [0, b_end) of seq_tiles (same value in every lane)
+template <bool MQ, int NCT>
+__device__ __forceinline__ long long tiles_before(const DecodeArgs& a, int b_end)
 {
     long long s = 0;
     for (int c = 0; c < b_end; c += kWave) {
         const int b = c + __lane_id();
-        s += wave_sum_i(b < b_end ? tiles_of(ctx[b]) : 0);
+        s += wave_sum_w<MQ>(b < b_end ? seq_tiles<MQ, NCT>(a, b) : 0);
     }
     return s;
 }
 
-// Sequence whose units contain linear tile x of the (b, hg, tile) list
-// (ngroups head groups per sequence); returns b and the tile count of the
-// sequences before it.
-__device__ __forceinline__ void locate_tile(const int32_t* ctx, int B, int ngroups, long long x,
+// Sequence whose units contain linear tile x of the (b, unit, tile) list
+// (ngroups head groups per sequence); returns b and the tiles per head
+// group of the sequences before it.
+template <bool MQ, int NCT>
+__device__ __forceinline__ void locate_tile(const DecodeArgs& a, int ngroups, long long x,
                                             int& b_out, long long& before_out)
 {
     long long base = 0;
-    for (int c = 0; c < B; c += kWave) {
+    for (int c = 0; c < a.B; c += kWave) {
         const int b = c + __lane_id();
-        const int n = b < B ? tiles_of(ctx[b]) : 0;
-        const int incl = wave_inclusive_scan(n);
+        const long long n = b < a.B ? seq_tiles<MQ, NCT>(a, b) : 0;
+        const long long incl =
+            MQ ? wave_inclusive_scan_ll(n) : (long long)wave_inclusive_scan((int)n);
         const unsigned long long hit = __ballot((base + incl) * ngroups > x);
         if (hit) {
             const int l = __builtin_ctzll(hit);
-            const int excl = __builtin_amdgcn_readlane(incl - n, l);
             b_out = c + l;
-            before_out = base + excl;
+            before_out = base + readlane_ll(incl - n, l);
             return;
         }
-        base += __builtin_amdgcn_readlane(incl, kWave - 1);
+        base += readlane_ll(incl, kWave - 1);
     }
-    b_out = B;
+    b_out = a.B;
     before_out = base;
 }
 
@@ -540,7 +650,7 @@ __device__ __forceinline__ long long range_start(long long r, long long total, l
     return (long long)__builtin_floor((double)(r * total) / (double)R);
 }
 
-template <int D, int BS, int FP8, int NT>
+template <int D, int BS, int FP8, int NT, int NCT, bool MQ>
 __global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 {
@@ -555,71 +665,117 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const int HG = ws.head_group;
     const int ngroups = a.Hkv / HG;
     const int G = a.G;
-    const long long total = tiles_before(a.context_lens, a.B) * ngroups;
+    constexpr int kCols = 16 * NCT;                  // MQ columns per wave
+    const int cpw = MQ ? kCols : G;                  // workspace rows per wave
+    const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
     if (r0 >= r1)
         return;
     int b;
     long long before;
-    locate_tile(a.context_lens, a.B, ngroups, r0, b, before);
+    locate_tile<MQ, NCT>(a, ngroups, r0, b, before);
     int T = a.context_lens[b];
     int n = tiles_of(T);
-    int hg = (int)((r0 - before * ngroups) / n);
-    unsigned char* lds = lds_all + wave * C::LDS_BYTES;
-    const int rows_per_slot = HG * G;
+    int ncg = col_groups<MQ, NCT>(a, b);
+    int u = (int)((r0 - before * ngroups) / n);      // unit of b: hg * ncg + cg
+    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, FP8, NCT>();
+    const int rows_per_slot = HG * cpw;
     long long x = r0;
     int piece = 0;
     while (true) {
-        const long long ustart = before * ngroups + (long long)hg * n;
+        const long long ustart = before * ngroups + (long long)u * n;
         const long long uend = ustart + n;
         const long long pend = uend < r1 ? uend : r1;
         const int t_begin = (int)(x - ustart) * kTile;
         const int t_end = min(T, (int)(pend - ustart) * kTile);
+        const int hg = MQ ? u / ncg : u;
+        const int cg = MQ ? u - hg * ncg : 0;
         const int h = hg * HG + wave;
-        RangeAcc<D> acc;
-        attend_range<D, BS, FP8, NT>(a, lds, b, h, t_begin, t_end, acc);
-        float inv, lse;
-        finish_range<D>(acc, inv, lse);
-        if (r16 < G) {
-            const int hq = h * G + r16;
-            if (x == ustart && pend == uend) {
-                store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, acc, inv);
-                if (a.lse_out && q4 == 0)
-                    a.lse_out[(size_t)b * a.Hq + hq] = lse;
-            } else {
-                const size_t slot = 2 * (size_t)r + (piece == 0 ? 0 : 1);
-                const size_t row = slot * rows_per_slot + wave * G + r16;
-                store_row<D>(ws.part_out + row * D, acc, inv);
-                if (q4 == 0)
-                    ws.part_lse[row] = lse;
+        const bool whole = x == ustart && pend == uend;
+        const size_t slot = 2 * (size_t)r + (piece == 0 ? 0 : 1);
+        if (!MQ) {
+            RangeAcc<D> acc[1];
+            attend_range<D, BS, FP8, NT, 1, false>(a, lds, b, h, t_begin, t_end,
+                                                   decode_cols(a, b, h, D), acc);
+            float inv, lse;
+            finish_range<D>(acc[0], inv, lse);
+            if (r16 < G) {
+                const int hq = h * G + r16;
+                if (whole) {
+                    store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, acc[0], inv);
+                    if (a.lse_out && q4 == 0)
+                        a.lse_out[(size_t)b * a.Hq + hq] = lse;
+                } else {
+                    const size_t row = slot * rows_per_slot + wave * G + r16;
+                    store_row<D>(ws.part_out + row * D, acc[0], inv);
+                    if (q4 == 0)
+                        ws.part_lse[row] = lse;
+                }
+            }
+        } else {
+            const int qs = a.query_start[b];
+            const int q = a.query_start[b + 1] - qs;
+            Cols<NCT> cs;
+            int qrow[NCT], hq[NCT];
+#pragma unroll
+            for (int j = 0; j < NCT; ++j) {
+                const int c = cg * kCols + 16 * j + r16;
+                const int i = c / G;
+                cs.live[j] = i < q;
+                qrow[j] = qs + (cs.live[j] ? i : 0);
+                hq[j] = h * G + (c - i * G);
+                cs.qrow[j] = a.query + ((size_t)qrow[j] * a.Hq + hq[j]) * D;
+                cs.lim[j] = T - q + i + 1;
+            }
+            cs.mask_from = T - q + (cg * kCols) / G + 1;
+            RangeAcc<D> acc[NCT];
+            attend_range<D, BS, FP8, NT, NCT, true>(a, lds, b, h, t_begin, t_end, cs, acc);
+#pragma unroll
+            for (int j = 0; j < NCT; ++j) {
+                float inv, lse;
+                finish_range<D>(acc[j], inv, lse);
+                if (!cs.live[j])
+                    continue;
+                if (whole) {
+                    const size_t orow = (size_t)qrow[j] * a.Hq + hq[j];
+                    store_row<D>(a.out + orow * D, acc[j], inv);
+                    if (a.lse_out && q4 == 0)
+                        a.lse_out[orow] = lse;
+                } else {
+                    const size_t row = slot * rows_per_slot + wave * kCols + 16 * j + r16;
+                    store_row<D>(ws.part_out + row * D, acc[j], inv);
+                    if (q4 == 0)
+                        ws.part_lse[row] = lse;
+                }
             }
         }
         ++piece;
         x = pend;
         if (x >= r1)
             break;
-        if (++hg == ngroups) {          // next sequence with a non-empty context
-            hg = 0;
-            before += n;
+        if (++u == ngroups * ncg) {     // next sequence with a non-empty unit
+            u = 0;
+            before += (long long)n * ncg;
             do {
                 ++b;
                 T = a.context_lens[b];
                 n = tiles_of(T);
-            } while (n == 0);
+                ncg = col_groups<MQ, NCT>(a, b);
+            } while (n == 0 || ncg == 0);
         }
     }
 }
 
-// One wave per output row (b, hq): merges the pieces of its unit
-// (b, head group of hq) when several work-groups shared it, writes zeros /
-// -inf for an empty sequence, and leaves rows that one group finished
-// alone untouched.  Lane (p, c) owns four output elements (column c) and
-// every npg-th piece starting at p; the npg partial sums meet through
-// lane butterflies.
+// One wave per output row (b, hq) -- (new row, hq) with several new tokens:
+// merges the pieces of its unit when several work-groups shared it, writes
+// zeros / -inf for an empty sequence, and leaves rows that one group
+// finished alone untouched.  Lane (p, c) owns four output elements
+// (column c) and every npg-th piece starting at p; the npg partial sums
+// meet through lane butterflies.
 constexpr int kMergeWaves = 4;
 
-template <int D>
+template <int D, int NCT, bool MQ>
 __global__ __launch_bounds__(kMergeWaves * kWave)
 void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
 {
@@ -627,16 +783,35 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     constexpr int npg = kWave / cols;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long row = (long long)blockIdx.x * kMergeWaves + wave;     // b * Hq + hq
-    if (row >= (long long)a.B * a.Hq)
+    const long long row = (long long)blockIdx.x * kMergeWaves + wave;
+    const int nrows = MQ ? a.total_rows : a.B;
+    if (row >= (long long)nrows * a.Hq)
         return;
-    const int b = (int)(row / a.Hq);
+    const int qr = (int)(row / a.Hq);                // sequence, or new-token row
     const int hq = (int)(row % a.Hq);
     const int G = a.G;
+    int b = qr;
+    int col = hq % G;                                // column of kv head h
+    if (MQ) {
+        b = a.B;
+        for (int c = 0; c < a.B; c += kWave) {
+            const int bb = c + lane;
+            const unsigned long long hit = __ballot(bb < a.B && a.query_start[bb + 1] > qr);
+            if (hit) {
+                b = c + __builtin_ctzll(hit);
+                break;
+            }
+        }
+        if (b >= a.B)
+            return;                                  // row past query_start[B]
+        col += (qr - a.query_start[b]) * G;
+    }
+    const int cpw = MQ ? 16 * NCT : G;
+    const int cg = col / cpw;
     const int HG = ws.head_group;
     const int h = hq / G;
     const int hg = h / HG;
-    const int in_slot = (h % HG) * G + hq % G;       // row index inside a slot
+    const int in_slot = (h % HG) * cpw + col % cpw;  // row index inside a slot
     const int ngroups = a.Hkv / HG;
     const int n = tiles_of(a.context_lens[b]);
     float* o = a.out + (size_t)row * D;
@@ -651,13 +826,14 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     long long total = 0, before = 0;
     for (int c = 0; c < a.B; c += kWave) {
         const int bb = c + lane;
-        const int nn = bb < a.B ? tiles_of(a.context_lens[bb]) : 0;
-        total += wave_sum_i(nn);
-        before += wave_sum_i(bb < b ? nn : 0);
+        const long long nn = bb < a.B ? seq_tiles<MQ, NCT>(a, bb) : 0;
+        total += wave_sum_w<MQ>(nn);
+        before += wave_sum_w<MQ>(bb < b ? nn : 0);
     }
     total *= ngroups;
     const long long R = ws.ngroups_launched;
-    const long long ustart = before * ngroups + (long long)hg * n;
+    const long long ustart =
+        before * ngroups + (long long)(hg * col_groups<MQ, NCT>(a, b) + cg) * n;
     const long long ulast = ustart + n - 1;
     auto range_of = [&](long long x) {
         long long r = (long long)((double)x * (double)R / (double)total);
@@ -671,7 +847,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     const long long rl = range_of(ulast);
     if (rf == rl)
         return;
-    const int rows_per_slot = HG * G;
+    const int rows_per_slot = HG * cpw;
     // Groups between rf and rl with an empty range (fewer tiles than
     // groups) hold no piece of this unit.
     auto piece_row = [&](long long r) -> long long {
@@ -682,7 +858,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
         return slot * rows_per_slot + in_slot;
     };
     const int p0 = lane / cols;
-    const int col = lane % cols;
+    const int c4 = lane % cols;
     // one online pass (running max, rescaled sums) over this lane's
     // pieces, four pieces' loads in flight per step
     constexpr int kBatch = 4;
@@ -704,7 +880,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
             v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (pr[k] >= 0) {
                 l[k] = ws.part_lse[pr[k]];
-                v[k] = *(const f32x4*)(ws.part_out + pr[k] * D + 4 * col);
+                v[k] = *(const f32x4*)(ws.part_out + pr[k] * D + 4 * c4);
             }
         }
         float mb = l[0];
@@ -739,42 +915,46 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
             accv[e] += xor_shuffle(accv[e], k);
     }
     if (lane < cols)
-        *(f32x4*)(o + 4 * col) = accv * (1.0f / wsum);
+        *(f32x4*)(o + 4 * c4) = accv * (1.0f / wsum);
     if (a.lse_out && lane == 0)
         a.lse_out[row] = m + __logf(wsum);
 }
 
-template <int D, int BS, int FP8>
+template <int D, int BS, int FP8, int NCT, bool MQ>
 int balanced_occupancy(int head_group)
 {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8, 1>),
-            head_group * kWave, (size_t)head_group * Cfg<D, FP8>::LDS_BYTES) != hipSuccess)
+            &blocks,
+            reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8, 1, NCT, MQ>),
+            head_group * kWave, (size_t)head_group * wave_lds_bytes<D, FP8, NCT>())
+        != hipSuccess)
         return 0;
     return blocks;
 }
 
-template <int D, int BS, int FP8>
+template <int D, int BS, int FP8, int NCT, bool MQ>
 hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt,
                              hipStream_t stream)
 {
-    const size_t lds = (size_t)ws.head_group * Cfg<D, FP8>::LDS_BYTES;
+    const size_t lds = (size_t)ws.head_group * wave_lds_bytes<D, FP8, NCT>();
     const dim3 grid((unsigned)ws.ngroups_launched), block(ws.head_group * kWave);
     if (nt)
-        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 1>), grid, block, lds, stream, a,
-                           ws);
+        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 1, NCT, MQ>), grid, block, lds,
+                           stream, a, ws);
     else
-        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 0>), grid, block, lds, stream, a,
-                           ws);
+        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 0, NCT, MQ>), grid, block, lds,
+                           stream, a, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const long long rows = (long long)a.B * a.Hq;
+    const long long rows = (long long)(MQ ? a.total_rows : a.B) * a.Hq;
     const long long groups = (rows + kMergeWaves - 1) / kMergeWaves;
     if (groups > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((balanced_merge_kernel<D>), dim3((unsigned)groups),
+    if (groups == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((balanced_merge_kernel<D, NCT, MQ>), dim3((unsigned)groups),
                        dim3(kMergeWaves * kWave), 0, stream, a, ws);
     return hipGetLastError();
 }
@@ -817,8 +997,8 @@ int balanced_groups_per_cu(int D, int block_size, int kv_dtype, int head_group)
 {
 #define PKV_OCC(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1>(head_group)                \
-                             : balanced_occupancy<d, bs, 0>(head_group);
+        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1, 1, false>(head_group)      \
+                             : balanced_occupancy<d, bs, 0, 1, false>(head_group);
     PKV_OCC(128, 16)
     PKV_OCC(128, 32)
     PKV_OCC(64, 16)
@@ -832,13 +1012,50 @@ hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, in
 {
 #define PKV_BAL(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1>(a, ws, nt, stream)          \
-                             : launch_balanced_t<d, bs, 0>(a, ws, nt, stream);
+        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1, 1, false>(a, ws, nt, stream) \
+                             : launch_balanced_t<d, bs, 0, 1, false>(a, ws, nt, stream);
     PKV_BAL(128, 16)
     PKV_BAL(128, 32)
     PKV_BAL(64, 16)
     PKV_BAL(64, 32)
 #undef PKV_BAL
+    return hipErrorInvalidValue;
+}
+
+int multiquery_groups_per_cu(int D, int block_size, int kv_dtype, int head_group, int nct)
+{
+#define PKV_MQOCC(d, bs, n)                                                             \
+    if (D == d && block_size == bs && nct == n)                                        \
+        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1, n, true>(head_group)       \
+                             : balanced_occupancy<d, bs, 0, n, true>(head_group);
+    PKV_MQOCC(128, 16, 1)
+    PKV_MQOCC(128, 32, 1)
+    PKV_MQOCC(64, 16, 1)
+    PKV_MQOCC(64, 32, 1)
+    PKV_MQOCC(128, 16, 2)
+    PKV_MQOCC(128, 32, 2)
+    PKV_MQOCC(64, 16, 2)
+    PKV_MQOCC(64, 32, 2)
+#undef PKV_MQOCC
+    return 0;
+}
+
+hipError_t launch_multiquery(const DecodeArgs& a, const BalanceArgs& ws, int D, int block_size,
+                             int kv_dtype, int nct, bool nt, hipStream_t stream)
+{
+#define PKV_MQ(d, bs, n)                                                                \
+    if (D == d && block_size == bs && nct == n)                                        \
+        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1, n, true>(a, ws, nt, stream)  \
+                             : launch_balanced_t<d, bs, 0, n, true>(a, ws, nt, stream);
+    PKV_MQ(128, 16, 1)
+    PKV_MQ(128, 32, 1)
+    PKV_MQ(64, 16, 1)
+    PKV_MQ(64, 32, 1)
+    PKV_MQ(128, 16, 2)
+    PKV_MQ(128, 32, 2)
+    PKV_MQ(64, 16, 2)
+    PKV_MQ(64, 32, 2)
+#undef PKV_MQ
     return hipErrorInvalidValue;
 }
 

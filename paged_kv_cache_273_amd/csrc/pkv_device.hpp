@@ -111,6 +111,40 @@ __device__ __forceinline__ int wave_sum_i(int v)
     return v;
 }
 
+// 64-bit forms of the two helpers above (two 32-bit lane exchanges).
+__device__ __forceinline__ long long shift_up_ll(long long v, int delta)
+{
+    const int lo = shift_up_i((int)(unsigned)(unsigned long long)v, delta);
+    const int hi = shift_up_i((int)((unsigned long long)v >> 32), delta);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+__device__ __forceinline__ long long wave_inclusive_scan_ll(long long v)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        v += shift_up_ll(v, d);
+    return v;
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const int lo = xor_shuffle_i((int)(unsigned)(unsigned long long)v, m);
+        const int hi = xor_shuffle_i((int)((unsigned long long)v >> 32), m);
+        v += (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+    }
+    return v;
+}
+
+__device__ __forceinline__ long long readlane_ll(long long v, int l)
+{
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(unsigned long long)v, l);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)((unsigned long long)v >> 32), l);
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll

@@ -31,7 +31,9 @@ struct DecodeArgs {
     float* lse_out;       // single pass, may be null
     float* partial_out;   // split
     float* partial_lse;   // split
+    const int32_t* query_start;  // several new tokens: [B + 1] row offsets, else null
     int32_t max_blocks, B, Hq, Hkv, G, split_tokens, max_splits;
+    int32_t total_rows;   // several new tokens: rows of query / out
     float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -42,6 +44,21 @@ struct BalanceArgs {
     float* part_lse;          // [2 * ngroups_launched, head_group * G]
     int32_t ngroups_launched; // work-groups (token ranges) of the decode launch
     int32_t head_group;       // kv heads per work-group (divides Hkv, <= 8)
+};
+
+// Several new K/V rows per sequence: rows query_start[b] .. query_start[b+1]-1
+// are positions T_b - q_b .. T_b - 1 of sequence b.
+struct WriteArgs {
+    const uint16_t* k_rows;
+    const uint16_t* v_rows;
+    const int32_t* query_start;
+    void* k_cache;
+    void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t max_blocks, B, max_query_len, Hkv, D, block_size, kv_dtype;
 };
 
 struct ReduceArgs {
@@ -60,6 +77,13 @@ hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtyp
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
                                   int block_size, int kv_dtype, bool nt, hipStream_t stream);
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+// Causal attention of several new tokens per sequence on the balanced
+// schedule; nct = 16-column MFMA tiles per wave (1 or 2).
+hipError_t launch_multiquery(const DecodeArgs& a, const BalanceArgs& ws, int D, int block_size,
+                             int kv_dtype, int nct, bool nt, hipStream_t stream);
+// resident work-groups per compute unit of the multi-query kernel (0 on error)
+int multiquery_groups_per_cu(int D, int block_size, int kv_dtype, int head_group, int nct);
 // kv heads per work-group of the balanced decode for Hkv kv heads
 int balanced_head_group(int Hkv);
 // resident work-groups per compute unit of the balanced decode (0 on error)

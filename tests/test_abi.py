@@ -29,7 +29,9 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["paged_kv_append", "paged_decode_attention",
                             "split_context_reduce", "paged_decode_attention_balanced",
-                            "paged_decode_workspace_size", "pkv_status_string"]), names
+                            "paged_decode_workspace_size", "paged_kv_write",
+                            "paged_multiquery_attention", "paged_multiquery_workspace_size",
+                            "pkv_status_string"]), names
 
 
 def test_library_exports_every_declared_symbol(pkv):
@@ -144,3 +146,76 @@ def test_append_rejects(pkv):
     assert L.paged_kv_append(0x1008, f, f, f, None, None, f, 4, f, 1, 2, 64, 16, 8, 0,
                              None) == -1
     assert L.paged_kv_append(f, f, f, f, None, None, f, 4, f, 0, 2, 64, 16, 8, 0, None) == 0
+
+
+def test_write_rejects(pkv):
+    L = pkv.lib()
+    f = 0x1000
+    # k_rows, v_rows, qs, k, v, ks, vs, bt, max_blocks, cl, B, max_q, Hkv, D, bs, nb, dt
+    ok = [f, f, f, f, f, None, None, f, 4, f, 2, 3, 2, 64, 16, 8, 0, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["kr", "vr", "qs", "k", "v", "ks", "vs", "bt", "mb", "cl", "B", "mq", "Hkv", "D",
+                 "bs", "nb", "dt", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.paged_kv_write(*a)
+
+    assert call(dt=1) == -1                  # fp8 without scales
+    assert call(D=80) == -2
+    assert call(bs=8) == -2
+    assert call(Hkv=0) == -1
+    assert call(mq=-1) == -1
+    assert call(qs=None) == -1
+    assert call(kr=0x1008) == -1             # misaligned rows
+    assert call(B=70000) == -2               # more sequences than one launch column holds
+    assert call(B=0) == 0
+    assert call(mq=0) == 0
+
+
+def _mq(pkv, **kw):
+    names = ["q", "qs", "rows", "mq", "k", "v", "ks", "vs", "bt", "mb", "cl", "B", "Hq", "Hkv",
+             "D", "bs", "nb", "dt", "scale", "ws", "wsb", "out", "lse", "stream"]
+    f = 0x1000
+    a = [f, f, 12, 4, f, f, None, None, f, 4, f, 3, 8, 2, 64, 16, 8, 0, 0.125, f, 1 << 20, f,
+         None, None]
+    for k, v in kw.items():
+        a[names.index(k)] = v
+    return pkv.lib().paged_multiquery_attention(*a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"Hq": 6, "Hkv": 4}, -1),
+    ({"D": 96}, -2),
+    ({"bs": 64}, -2),
+    ({"Hq": 64, "Hkv": 2}, -2),
+    ({"dt": 2}, -1),
+    ({"dt": 1}, -1),                     # fp8 without scales
+    ({"ws": None}, -1),
+    ({"ws": 0x1004}, -1),
+    ({"qs": None}, -1),
+    ({"mq": 0}, -1),                     # rows but no new tokens
+    ({"mq": -2}, -1),
+    ({"rows": -1}, -1),
+    ({"wsb": -5}, -1),
+    ({"mb": 1 << 22}, -2),
+    ({"scale": float("nan")}, -1),
+    ({"lse": 0x1002}, -1),               # misaligned lse
+])
+def test_multiquery_rejects(pkv, kw, status):
+    assert _mq(pkv, **kw) == status
+
+
+def test_multiquery_empty_is_a_no_op(pkv):
+    assert _mq(pkv, B=0) == 0
+    assert _mq(pkv, rows=0) == 0
+
+
+def test_multiquery_workspace_size_rejects(pkv):
+    L = pkv.lib()
+    assert L.paged_multiquery_workspace_size(6, 4, 64, 16, 0, 4) == -1
+    assert L.paged_multiquery_workspace_size(8, 2, 96, 16, 0, 4) == -2
+    assert L.paged_multiquery_workspace_size(8, 2, 64, 8, 0, 4) == -2
+    assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 7, 4) == -1
+    assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 0, -1) == -1
