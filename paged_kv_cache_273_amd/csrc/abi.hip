@@ -180,10 +180,28 @@ static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t k
     return cus * pkv::balanced_groups_per_cu(D, block_size, kv_dtype, hg);
 }
 
+// Partial slots (2 per work-group) of rows_per_group rows, then the cut
+// records at the next 16-byte boundary.
+static int64_t schedule_bytes(int ngroups, int64_t rows_per_group, int32_t D)
+{
+    const int64_t rows = (int64_t)2 * ngroups * rows_per_group;
+    const int64_t parts = rows * (D + 1) * (int64_t)sizeof(float);
+    return (parts + 15) / 16 * 16 + (int64_t)ngroups * sizeof(pkv::CutRecord);
+}
+
+static void carve_workspace(pkv::BalanceArgs& ws, void* workspace, int64_t rows_per_group,
+                            int32_t D)
+{
+    const int64_t rows = (int64_t)2 * ws.ngroups_launched * rows_per_group;
+    ws.part_out = (float*)workspace;
+    ws.part_lse = ws.part_out + (size_t)rows * D;
+    const int64_t parts = rows * (D + 1) * (int64_t)sizeof(float);
+    ws.cuts = (pkv::CutRecord*)((char*)workspace + (parts + 15) / 16 * 16);
+}
+
 static int64_t balanced_bytes(int ngroups, int32_t Hkv, int32_t G, int32_t D)
 {
-    const int64_t rows = (int64_t)2 * ngroups * pkv::balanced_head_group(Hkv) * G;
-    return rows * (D + 1) * (int64_t)sizeof(float);
+    return schedule_bytes(ngroups, (int64_t)pkv::balanced_head_group(Hkv) * G, D);
 }
 
 int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
@@ -261,8 +279,7 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv);
     ws.ngroups_launched = n;
-    ws.part_out = (float*)workspace;
-    ws.part_lse = ws.part_out + (size_t)2 * n * ws.head_group * G * D;
+    carve_workspace(ws, workspace, (int64_t)ws.head_group * G, D);
     // range boundaries are computed in double precision: keep
     // (tiles of the call) * (groups launched) below 2^52
     const int64_t ngroups = Hkv / ws.head_group;
@@ -340,8 +357,7 @@ static int mq_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtyp
 
 static int64_t mq_bytes(int ngroups, int32_t Hkv, int nct, int32_t D)
 {
-    const int64_t rows = (int64_t)2 * ngroups * pkv::balanced_head_group(Hkv) * 16 * nct;
-    return rows * (D + 1) * (int64_t)sizeof(float);
+    return schedule_bytes(ngroups, (int64_t)pkv::balanced_head_group(Hkv) * 16 * nct, D);
 }
 
 int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
@@ -426,8 +442,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv);
     ws.ngroups_launched = n;
-    ws.part_out = (float*)workspace;
-    ws.part_lse = ws.part_out + (size_t)2 * n * ws.head_group * 16 * nct * D;
+    carve_workspace(ws, workspace, (int64_t)ws.head_group * 16 * nct, D);
     // range boundaries in double precision: (tiles of the call) * (groups
     // launched) must stay below 2^52
     const int64_t ngroups = Hkv / ws.head_group;

@@ -183,7 +183,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     // Q^T operands: column r16 of tile j is this lane's query (zero if
     // dead); in registers for one column tile, in LDS for several.
     constexpr bool QLDS = NCT > 1;
-    volatile u32x4* qlds = (volatile u32x4*)(lds + C::LDS_BYTES);
+    typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
+    lds_u32x4* qlds = (lds_u32x4*)(lds + C::LDS_BYTES);
     bf16x8 qf[QLDS ? 1 : NCT][C::KSTEPS];
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
@@ -563,8 +564,9 @@ void decode_kernel(DecodeArgs a)
 // whatever the mix of context lengths.  A unit inside one group's range is
 // written straight to `out`; a unit cut by range boundaries leaves one
 // normalised partial per piece in the workspace (slot 2r for a group's
-// first piece, 2r+1 for its last) and balanced_merge_kernel combines them
-// with the log-sum-exp rule.
+// first piece, 2r+1 for its last), the group holding its first piece
+// records it (CutRecord), and balanced_merge_kernel combines the pieces of
+// every recorded unit with the log-sum-exp rule.
 //
 // Several new tokens per sequence (MQ): the columns of kv head h are the
 // pairs (new row i, head g) in the order c = i * G + g, cut into column
@@ -670,8 +672,12 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
-    if (r0 >= r1)
+    CutRecord cut = {-1, 0, 0, total, 0};
+    if (r0 >= r1) {
+        if (threadIdx.x == 0)
+            ws.cuts[r] = cut;
         return;
+    }
     int b;
     long long before;
     locate_tile<MQ, NCT>(a, ngroups, r0, b, before);
@@ -752,8 +758,14 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         }
         ++piece;
         x = pend;
-        if (x >= r1)
+        if (x >= r1) {
+            if (pend < uend && ustart >= r0) {   // this group holds the unit's first piece
+                cut.b = b;
+                cut.u = u;
+                cut.ustart = ustart;
+            }
             break;
+        }
         if (++u == ngroups * ncg) {     // next sequence with a non-empty unit
             u = 0;
             before += (long long)n * ncg;
@@ -765,14 +777,18 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
             } while (n == 0 || ncg == 0);
         }
     }
+    if (threadIdx.x == 0)
+        ws.cuts[r] = cut;
 }
 
-// One wave per output row (b, hq) -- (new row, hq) with several new tokens:
-// merges the pieces of its unit when several work-groups shared it, writes
-// zeros / -inf for an empty sequence, and leaves rows that one group
-// finished alone untouched.  Lane (p, c) owns four output elements
-// (column c) and every npg-th piece starting at p; the npg partial sums
-// meet through lane butterflies.
+// Merge of the recorded cut units.  Work-group (r, y) takes the unit that
+// work-group r of the main launch recorded and merges kMergeWaves of its
+// rows, one wave per row (row = kv head of the group x column).  Lane
+// (p, c) owns four output elements (column c) and every npg-th piece
+// starting at p; the npg partial sums meet through lane butterflies.
+// The extra column r = R writes out = 0, lse = -inf for the rows of empty
+// sequences (decode step only: with several new tokens an empty sequence
+// has no rows).
 constexpr int kMergeWaves = 4;
 
 template <int D, int NCT, bool MQ>
@@ -783,57 +799,57 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     constexpr int npg = kWave / cols;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long row = (long long)blockIdx.x * kMergeWaves + wave;
-    const int nrows = MQ ? a.total_rows : a.B;
-    if (row >= (long long)nrows * a.Hq)
-        return;
-    const int qr = (int)(row / a.Hq);                // sequence, or new-token row
-    const int hq = (int)(row % a.Hq);
+    const long long R = ws.ngroups_launched;
+    const int HG = ws.head_group;
     const int G = a.G;
-    int b = qr;
-    int col = hq % G;                                // column of kv head h
-    if (MQ) {
-        b = a.B;
-        for (int c = 0; c < a.B; c += kWave) {
-            const int bb = c + lane;
-            const unsigned long long hit = __ballot(bb < a.B && a.query_start[bb + 1] > qr);
-            if (hit) {
-                b = c + __builtin_ctzll(hit);
-                break;
+    constexpr int kCols = 16 * NCT;
+    const int cpw = MQ ? kCols : G;
+    if ((long long)blockIdx.x == R) {
+        if (MQ)
+            return;
+        for (int b = blockIdx.y; b < a.B; b += gridDim.y) {
+            if (a.context_lens[b] > 0)
+                continue;
+            for (int hq = wave; hq < a.Hq; hq += kMergeWaves) {
+                float* o = a.out + ((size_t)b * a.Hq + hq) * D;
+                for (int d = lane; d < D; d += kWave)
+                    o[d] = 0.f;
+                if (a.lse_out && lane == 0)
+                    a.lse_out[(size_t)b * a.Hq + hq] = -__builtin_inff();
             }
         }
-        if (b >= a.B)
-            return;                                  // row past query_start[B]
-        col += (qr - a.query_start[b]) * G;
-    }
-    const int cpw = MQ ? 16 * NCT : G;
-    const int cg = col / cpw;
-    const int HG = ws.head_group;
-    const int h = hq / G;
-    const int hg = h / HG;
-    const int in_slot = (h % HG) * cpw + col % cpw;  // row index inside a slot
-    const int ngroups = a.Hkv / HG;
-    const int n = tiles_of(a.context_lens[b]);
-    float* o = a.out + (size_t)row * D;
-    if (n == 0) {
-        for (int d = lane; d < D; d += kWave)
-            o[d] = 0.f;
-        if (a.lse_out && lane == 0)
-            a.lse_out[row] = -__builtin_inff();
         return;
     }
-    // tiles of all sequences and of the sequences before b, in one pass
-    long long total = 0, before = 0;
-    for (int c = 0; c < a.B; c += kWave) {
-        const int bb = c + lane;
-        const long long nn = bb < a.B ? seq_tiles<MQ, NCT>(a, bb) : 0;
-        total += wave_sum_w<MQ>(nn);
-        before += wave_sum_w<MQ>(bb < b ? nn : 0);
+    const CutRecord* rec = ws.cuts + blockIdx.x;
+    const int b = rec->b;
+    if (b < 0)
+        return;
+    const int in_slot = blockIdx.y * kMergeWaves + wave;   // w * cpw + column
+    if (in_slot >= HG * cpw)
+        return;
+    const int u = rec->u;
+    const int ncg = col_groups<MQ, NCT>(a, b);
+    const int hg = MQ ? u / ncg : u;
+    const int cg = MQ ? u - hg * ncg : 0;
+    const int h = hg * HG + in_slot / cpw;
+    const int cc = in_slot % cpw;
+    size_t orow;
+    if (!MQ) {
+        if (cc >= G)
+            return;
+        orow = (size_t)b * a.Hq + h * G + cc;
+    } else {
+        const int col = cg * kCols + cc;
+        const int i = col / G;
+        const int qs = a.query_start[b];
+        if (i >= a.query_start[b + 1] - qs)
+            return;
+        orow = (size_t)(qs + i) * a.Hq + h * G + (col - i * G);
     }
-    total *= ngroups;
-    const long long R = ws.ngroups_launched;
-    const long long ustart =
-        before * ngroups + (long long)(hg * col_groups<MQ, NCT>(a, b) + cg) * n;
+    float* o = a.out + orow * D;
+    const int n = tiles_of(a.context_lens[b]);
+    const long long total = rec->total;
+    const long long ustart = rec->ustart;
     const long long ulast = ustart + n - 1;
     auto range_of = [&](long long x) {
         long long r = (long long)((double)x * (double)R / (double)total);
@@ -843,10 +859,8 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
             --r;
         return r;
     };
-    const long long rf = range_of(ustart);
+    const long long rf = blockIdx.x;
     const long long rl = range_of(ulast);
-    if (rf == rl)
-        return;
     const int rows_per_slot = HG * cpw;
     // Groups between rf and rl with an empty range (fewer tiles than
     // groups) hold no piece of this unit.
@@ -917,7 +931,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     if (lane < cols)
         *(f32x4*)(o + 4 * c4) = accv * (1.0f / wsum);
     if (a.lse_out && lane == 0)
-        a.lse_out[row] = m + __logf(wsum);
+        a.lse_out[orow] = m + __logf(wsum);
 }
 
 template <int D, int BS, int FP8, int NCT, bool MQ>
@@ -948,14 +962,11 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const long long rows = (long long)(MQ ? a.total_rows : a.B) * a.Hq;
-    const long long groups = (rows + kMergeWaves - 1) / kMergeWaves;
-    if (groups > 0x7FFFFFFFLL)
-        return hipErrorInvalidConfiguration;
-    if (groups == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL((balanced_merge_kernel<D, NCT, MQ>), dim3((unsigned)groups),
-                       dim3(kMergeWaves * kWave), 0, stream, a, ws);
+    const int cpw = MQ ? 16 * NCT : a.G;
+    const unsigned ychunks = (unsigned)((ws.head_group * cpw + kMergeWaves - 1) / kMergeWaves);
+    const dim3 mgrid((unsigned)ws.ngroups_launched + 1, ychunks);
+    hipLaunchKernelGGL((balanced_merge_kernel<D, NCT, MQ>), mgrid, dim3(kMergeWaves * kWave), 0,
+                       stream, a, ws);
     return hipGetLastError();
 }
 

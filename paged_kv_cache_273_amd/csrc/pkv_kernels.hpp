@@ -37,11 +37,23 @@ struct DecodeArgs {
     float scale_log2;     // softmax scale * log2(e)
 };
 
-// Workspace of the balanced decode: 2 partial slots per launched
-// work-group, each with head_group * G rows of D floats and as many lse.
+// The unit a work-group starts but leaves unfinished (b < 0: none).
+struct CutRecord {
+    int32_t b;                // sequence
+    int32_t u;                // unit of the sequence (head group, column group)
+    long long ustart;         // linear index of the unit's first tile
+    long long total;          // tiles of the whole call
+    long long pad;
+};
+
+// Workspace of the balanced schedule: 2 partial slots per launched
+// work-group, each with head_group * C rows (C = G for a decode step,
+// 16 * column tiles with several new tokens) of D floats and as many lse,
+// then one CutRecord per work-group.
 struct BalanceArgs {
-    float* part_out;          // [2 * ngroups_launched, head_group * G, D]
-    float* part_lse;          // [2 * ngroups_launched, head_group * G]
+    float* part_out;          // [2 * ngroups_launched, head_group * C, D]
+    float* part_lse;          // [2 * ngroups_launched, head_group * C]
+    CutRecord* cuts;          // [ngroups_launched], 16-byte aligned
     int32_t ngroups_launched; // work-groups (token ranges) of the decode launch
     int32_t head_group;       // kv heads per work-group (divides Hkv, <= 8)
 };
