@@ -89,6 +89,45 @@ def test_every_planted_mistake_is_caught(tmp_path):
     assert not survivors, f"pins did not catch: {survivors}"
 
 
+BM_SRC = os.path.join(ROOT, "oracle", "block_manager.py")
+BM_MUTANTS = [
+    ("key_not_cumulative", "return (self.ns, tuple(toks[:end]))",
+     "return (self.ns, tuple(toks[end - self.bs:end]))"),
+    ("last_token_reused", "for j in range((len(toks) - 1) // bs):",
+     "for j in range(len(toks) // bs):"),
+    ("evicts_newest", "victim = self.lru.pop(0)", "victim = self.lru.pop()"),
+    ("releases_first_block_first", "for b in reversed(self.tables.pop(seq)):",
+     "for b in self.tables.pop(seq):"),
+    ("no_copy_on_write", "elif self.ref[table[-1]] > 1:", "elif False:"),
+    ("highest_free_block", "return self.free.pop(0)", "return self.free.pop()"),
+    ("evicted_key_kept", "del self.cache[self.key[victim]]", "pass"),
+    ("evicts_before_free", "if self.free:\n            self.free.sort()",
+     "if self.free and not self.lru:\n            self.free.sort()"),
+]
+
+
+def _run_bm_mutant(tmpdir, name, old, new):
+    src = open(BM_SRC).read()
+    assert src.count(old) >= 1, f"{name}: pattern not found"
+    path = os.path.join(tmpdir, f"bm_{name}.py")
+    open(path, "w").write(src.replace(old, new))
+    env = dict(os.environ, PKV_ORACLE_BM=path)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_block_manager.py"], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+def test_every_planted_block_manager_mistake_is_caught(tmp_path):
+    with cf.ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        futs = [ex.submit(_run_bm_mutant, str(tmp_path), *m) for m in BM_MUTANTS]
+        results = [f.result() for f in futs]
+    survivors = [name for name, rc in results if rc == 0]
+    assert not survivors, f"block-manager pins did not catch: {survivors}"
+
+
 def test_unmutated_copy_passes(tmp_path):
     name, rc = _run_mutant(str(tmp_path), "identity", "#include <math.h>", "#include <math.h>")
+    assert rc == 0
+    name, rc = _run_bm_mutant(str(tmp_path), "identity", "class NoSpace", "class NoSpace")
     assert rc == 0
