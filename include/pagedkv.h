@@ -76,7 +76,10 @@ enum pkv_status {
     PKV_OK = 0,
     PKV_EINVAL = -1,        /* bad scalar, null or misaligned pointer      */
     PKV_EUNSUPPORTED = -2,  /* shape outside the compiled kernel set       */
-    PKV_ELAUNCH = -3        /* the HIP runtime reported a launch failure   */
+    PKV_ELAUNCH = -3,       /* the HIP runtime reported a launch failure   */
+    PKV_ENOSPACE = -4,      /* block manager: not enough free or evictable
+                               blocks (nothing changed)                    */
+    PKV_ENOMEM = -5         /* block manager: host allocation failed       */
 };
 
 enum pkv_dtype {

@@ -25,13 +25,17 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, -1, -2, -3
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH, PKV_ENOSPACE, PKV_ENOMEM = 0, -1, -2, -3, -4, -5
 PKV_BF16, PKV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "paged_decode_attention_balanced", "paged_decode_workspace_size",
            "paged_kv_write", "paged_multiquery_attention", "paged_multiquery_workspace_size",
-           "pkv_status_string")
+           "pkv_status_string",
+           # host block manager (include/pkv_block_manager.h; binding in block_manager.py)
+           "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append", "pkv_bm_fork",
+           "pkv_bm_release", "pkv_bm_take_copies", "pkv_bm_context_len", "pkv_bm_table",
+           "pkv_bm_export", "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru")
 
 
 class PagedKVError(RuntimeError):

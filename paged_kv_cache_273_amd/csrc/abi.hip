@@ -63,6 +63,8 @@ const char* pkv_status_string(int status)
     case PKV_EINVAL: return "invalid argument";
     case PKV_EUNSUPPORTED: return "unsupported shape";
     case PKV_ELAUNCH: return "kernel launch failed";
+    case PKV_ENOSPACE: return "no free block";
+    case PKV_ENOMEM: return "host allocation failed";
     default: return "unknown status";
     }
 }

@@ -8,14 +8,21 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pagedkv.h", "pkv_block_manager.h")]
 
 
-def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+def _declared(headers=HEADERS):
+    names = []
+    for h in headers:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))
+
+
+def test_every_header_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(
+        os.path.basename(h) for h in HEADERS)
 
 
 @pytest.fixture(scope="module")
@@ -26,12 +33,20 @@ def pkv():
 
 
 def test_header_declares_the_boundary():
-    names = _declared()
+    names = _declared(HEADERS[:1])
     assert names == sorted(["paged_kv_append", "paged_decode_attention",
                             "split_context_reduce", "paged_decode_attention_balanced",
                             "paged_decode_workspace_size", "paged_kv_write",
                             "paged_multiquery_attention", "paged_multiquery_workspace_size",
                             "pkv_status_string"]), names
+
+
+def test_block_manager_header_declares_its_calls():
+    names = _declared(HEADERS[1:])
+    assert names == sorted(["pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append",
+                            "pkv_bm_fork", "pkv_bm_release", "pkv_bm_take_copies",
+                            "pkv_bm_context_len", "pkv_bm_table", "pkv_bm_export",
+                            "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru"]), names
 
 
 def test_library_exports_every_declared_symbol(pkv):
@@ -47,6 +62,8 @@ def test_status_strings(pkv):
     assert L.pkv_status_string(-1) == b"invalid argument"
     assert L.pkv_status_string(-2) == b"unsupported shape"
     assert L.pkv_status_string(-3) == b"kernel launch failed"
+    assert L.pkv_status_string(-4) == b"no free block"
+    assert L.pkv_status_string(-5) == b"host allocation failed"
 
 
 def _decode(pkv, **kw):
