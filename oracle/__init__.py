@@ -64,6 +64,9 @@ def lib():
         "orc_split_reduce": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
         "orc_fp8_block_scales": (None, [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
         "orc_fp8_quantize_pool": (None, [_P, _P, _I32, _I32, _I32, _I32, _P]),
+        "orc_gather_blocks": (None, [_P, _P, _I32, _I64, _P]),
+        "orc_scatter_blocks": (None, [_P, _P, _I32, _I64, _P]),
+        "orc_copy_blocks": (None, [_P, _P, _P, _I32, _I64]),
         "orc_write_tokens": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
                                     _I32, _I32, _I32]),
         "orc_multiquery_attention": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
@@ -249,3 +252,29 @@ def multiquery_attention(query, query_start, k_cache, v_cache, block_tables, con
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out, lse
+
+
+# ---------------------------------------------------------------- whole blocks
+def _block_bytes(pool):
+    return int(pool[0].nbytes) if pool.shape[0] else 0
+
+
+def gather_blocks(pool, ids):
+    """pool [num_blocks, ...] -> [n, ...] with out[i] = pool[ids[i]]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = np.empty((ids.size,) + pool.shape[1:], dtype=pool.dtype)
+    lib().orc_gather_blocks(_ptr(pool), _ptr(ids), ids.size, _block_bytes(pool), _ptr(out))
+    return out
+
+
+def scatter_blocks(blocks, ids, pool):
+    """In place: pool[ids[i]] = blocks[i]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    lib().orc_scatter_blocks(_ptr(blocks), _ptr(ids), ids.size, _block_bytes(pool), _ptr(pool))
+
+
+def copy_blocks(pool, src, dst):
+    """In place: pool[dst[i]] = pool[src[i]]."""
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    lib().orc_copy_blocks(_ptr(pool), _ptr(src), _ptr(dst), src.size, _block_bytes(pool))

@@ -551,6 +551,46 @@ int32_t orc_multiquery_attention(const uint16_t* query, const int32_t* query_sta
 }
 
 /* ------------------------------------------------------------------ */
+/* Whole-block moves.  [C] "When the cache fills" (preempting a sequence by */
+/* swapping its cache to host memory) and "Offload"; [A] anti-pattern (5)   */
+/* (offloading inactive sessions to CPU memory); [B] "PagedAttention"       */
+/* block sharing, whose copy-on-write needs a block copy.  A block is        */
+/* block_bytes contiguous bytes of a pool (K or V codes, or one block's     */
+/* scales).                                                                 */
+/* ------------------------------------------------------------------ */
+
+/* out[i] = pool[ids[i]] for i < n. */
+void orc_gather_blocks(const void* pool, const int32_t* ids, int32_t n, int64_t block_bytes,
+                       void* out)
+{
+    int32_t i;
+    for (i = 0; i < n; ++i)
+        memcpy((char*)out + (int64_t)i * block_bytes,
+               (const char*)pool + (int64_t)ids[i] * block_bytes, (size_t)block_bytes);
+}
+
+/* pool[ids[i]] = in[i] for i < n. */
+void orc_scatter_blocks(const void* in, const int32_t* ids, int32_t n, int64_t block_bytes,
+                        void* pool)
+{
+    int32_t i;
+    for (i = 0; i < n; ++i)
+        memcpy((char*)pool + (int64_t)ids[i] * block_bytes,
+               (const char*)in + (int64_t)i * block_bytes, (size_t)block_bytes);
+}
+
+/* pool[dst[i]] = pool[src[i]] for i < n (no block is both a source and a
+ * destination). */
+void orc_copy_blocks(void* pool, const int32_t* src, const int32_t* dst, int32_t n,
+                     int64_t block_bytes)
+{
+    int32_t i;
+    for (i = 0; i < n; ++i)
+        memcpy((char*)pool + (int64_t)dst[i] * block_bytes,
+               (const char*)pool + (int64_t)src[i] * block_bytes, (size_t)block_bytes);
+}
+
+/* ------------------------------------------------------------------ */
 /* FP8 cache population (used to build fp8 test caches).               */
 /* [B] "FP8 KV cache": a dynamic scale factor per head.  Reading: one    */
 /* binary32 scale per (physical block, kv head), amax / 448 over the     */

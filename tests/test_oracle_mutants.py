@@ -16,7 +16,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_formula.py", "tests/test_oracle_fp8.py",
-        "tests/test_oracle_attention.py", "tests/test_oracle_multiquery.py"]
+        "tests/test_oracle_attention.py", "tests/test_oracle_multiquery.py",
+        "tests/test_oracle_blocks.py"]
 
 # (name, original text, planted text, occurrence count expected)
 MUTANTS = [
@@ -60,6 +61,12 @@ MUTANTS = [
     ("mq_query_row_of_sequence", "const uint16_t* qrow = query + row * Hq * D;",
      "const uint16_t* qrow = query + (int64_t)b * Hq * D;"),
     ("write_rows_reversed", "int32_t t = T - q + i;", "int32_t t = T - 1 - i;"),
+    ("gather_by_position", "(const char*)pool + (int64_t)ids[i] * block_bytes",
+     "(const char*)pool + (int64_t)i * block_bytes"),
+    ("scatter_by_position", "memcpy((char*)pool + (int64_t)ids[i] * block_bytes,",
+     "memcpy((char*)pool + (int64_t)i * block_bytes,"),
+    ("copy_reversed", "memcpy((char*)pool + (int64_t)dst[i] * block_bytes,\n               (const char*)pool + (int64_t)src[i] * block_bytes",
+     "memcpy((char*)pool + (int64_t)src[i] * block_bytes,\n               (const char*)pool + (int64_t)dst[i] * block_bytes"),
     ("write_v_with_k_scale", "orc_e4m3_quantize(v_rows[src], v_scale[",
      "orc_e4m3_quantize(v_rows[src], k_scale["),
 ]
