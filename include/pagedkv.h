@@ -319,6 +319,49 @@ int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D,
                                         int32_t block_size, int32_t kv_dtype,
                                         int32_t max_query_len);
 
+/*
+ * ---------------------------------------------------------------------
+ * Whole-block moves ([C] "When the cache fills": preempting a sequence by
+ * swapping its cache to host memory and back; "Offload"; [B]
+ * "PagedAttention" block sharing, whose copy-on-write copies a block).
+ * A block is block_size * Hkv * D * (2 bf16 | 1 fp8) contiguous bytes of
+ * k_cache (and of v_cache), plus its Hkv scales of k_scale / v_scale for
+ * fp8.  The block size in bytes must be a multiple of 16.  Buffers may be
+ * device memory or pinned host memory the device can address
+ * (hipHostMalloc); a move then streams over the host link.  Block id
+ * CONTENTS are device-side preconditions: ids in [0, num_blocks), and for
+ * copies no block both a source and a destination, no destination twice.
+ * Returns PKV_EINVAL for null / misaligned (16 bytes) pointers or bad
+ * sizes, PKV_EUNSUPPORTED if the block size in bytes is not a multiple of
+ * 16; n == 0 is a no-op.
+ * ---------------------------------------------------------------------
+ */
+
+/* k_out[i] = k_cache[block_ids[i]] (and V, and fp8 scales), i < n:
+ * k_out, v_out [n, block_size, Hkv, D]; scale outputs [n, Hkv]. */
+int paged_kv_gather_blocks(const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_ids, int32_t n,
+                           int32_t block_size, int32_t Hkv, int32_t D,
+                           int32_t num_blocks, int32_t kv_dtype,
+                           void* k_out, void* v_out,
+                           float* k_scale_out, float* v_scale_out, void* stream);
+
+/* k_cache[block_ids[i]] = k_in[i] (and V, and fp8 scales), i < n. */
+int paged_kv_scatter_blocks(const void* k_in, const void* v_in,
+                            const float* k_scale_in, const float* v_scale_in,
+                            const int32_t* block_ids, int32_t n,
+                            int32_t block_size, int32_t Hkv, int32_t D,
+                            int32_t num_blocks, int32_t kv_dtype,
+                            void* k_cache, void* v_cache,
+                            float* k_scale, float* v_scale, void* stream);
+
+/* k_cache[dst_ids[i]] = k_cache[src_ids[i]] (and V, and fp8 scales). */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                         int32_t block_size, int32_t Hkv, int32_t D,
+                         int32_t num_blocks, int32_t kv_dtype, void* stream);
+
 /* Human-readable name of a pkv_status value (static storage). */
 const char* pkv_status_string(int status);
 

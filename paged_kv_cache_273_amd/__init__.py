@@ -31,7 +31,8 @@ PKV_BF16, PKV_FP8_E4M3 = 0, 1
 EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "paged_decode_attention_balanced", "paged_decode_workspace_size",
            "paged_kv_write", "paged_multiquery_attention", "paged_multiquery_workspace_size",
-           "pkv_status_string",
+           "pkv_status_string", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
+           "paged_kv_copy_blocks",
            # host block manager (include/pkv_block_manager.h; binding in block_manager.py)
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append", "pkv_bm_fork",
            "pkv_bm_release", "pkv_bm_take_copies", "pkv_bm_context_len", "pkv_bm_table",
@@ -70,6 +71,11 @@ def _load(path=LIB_PATH):
                                              I, C.c_float, P, C.c_int64, P, P, P]
     L.paged_multiquery_workspace_size.restype = C.c_int64
     L.paged_multiquery_workspace_size.argtypes = [I, I, I, I, I, I]
+    for name in ("paged_kv_gather_blocks", "paged_kv_scatter_blocks"):
+        getattr(L, name).restype = C.c_int
+        getattr(L, name).argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
+    L.paged_kv_copy_blocks.restype = C.c_int
+    L.paged_kv_copy_blocks.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
     L.pkv_status_string.restype = C.c_char_p
     L.pkv_status_string.argtypes = [C.c_int]
     return L
@@ -295,6 +301,65 @@ def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_table
         _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out), _stream(stream))
     _check("paged_multiquery_attention", st)
     return out
+
+
+def _any_ptr(t):
+    """Pointer of a device tensor or of a pinned host tensor (both are
+    addressable by the kernels)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("host buffers must be pinned (pin_memory=True)")
+    return t.data_ptr()
+
+
+def _move_shape(k_cache):
+    nb, bs, Hkv, D = k_cache.shape
+    return nb, bs, Hkv, D, _kv_dtype(k_cache)
+
+
+def paged_kv_gather_blocks(k_cache, v_cache, block_ids, k_out, v_out, *, k_scale=None,
+                           v_scale=None, k_scale_out=None, v_scale_out=None, stream=None):
+    """k_out[i] = k_cache[block_ids[i]] (and V, and fp8 scales).  Outputs may
+    be pinned host tensors (swap out / offload)."""
+    _need(block_ids, (torch.int32,), "block_ids")
+    nb, bs, Hkv, D, dt = _move_shape(k_cache)
+    st = _lib.paged_kv_gather_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _any_ptr(block_ids),
+        block_ids.numel(), bs, Hkv, D, nb, dt, _any_ptr(k_out), _any_ptr(v_out),
+        _any_ptr(k_scale_out), _any_ptr(v_scale_out), _stream(stream))
+    _check("paged_kv_gather_blocks", st)
+
+
+def paged_kv_scatter_blocks(k_in, v_in, block_ids, k_cache, v_cache, *, k_scale_in=None,
+                            v_scale_in=None, k_scale=None, v_scale=None, stream=None):
+    """k_cache[block_ids[i]] = k_in[i] (and V, and fp8 scales).  Inputs may be
+    pinned host tensors (swap in)."""
+    _need(block_ids, (torch.int32,), "block_ids")
+    nb, bs, Hkv, D, dt = _move_shape(k_cache)
+    st = _lib.paged_kv_scatter_blocks(
+        _any_ptr(k_in), _any_ptr(v_in), _any_ptr(k_scale_in), _any_ptr(v_scale_in),
+        _any_ptr(block_ids), block_ids.numel(), bs, Hkv, D, nb, dt, _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _stream(stream))
+    _check("paged_kv_scatter_blocks", st)
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, src_ids, dst_ids, *, k_scale=None, v_scale=None,
+                         stream=None):
+    """k_cache[dst_ids[i]] = k_cache[src_ids[i]] (copy-on-write copies)."""
+    _need(src_ids, (torch.int32,), "src_ids")
+    _need(dst_ids, (torch.int32,), "dst_ids")
+    if src_ids.numel() != dst_ids.numel():
+        raise ValueError("src_ids and dst_ids differ in length")
+    nb, bs, Hkv, D, dt = _move_shape(k_cache)
+    st = _lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                   _any_ptr(src_ids), _any_ptr(dst_ids), src_ids.numel(), bs, Hkv,
+                                   D, nb, dt, _stream(stream))
+    _check("paged_kv_copy_blocks", st)
 
 
 def max_splits_for(max_context: int, split_tokens: int) -> int:

@@ -458,6 +458,114 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
                                            (hipStream_t)stream));
 }
 
+// Common checks of the block moves; fills block_bytes and scale_count.
+static int move_checks(int32_t n, int32_t block_size, int32_t Hkv, int32_t D, int32_t num_blocks,
+                       int32_t kv_dtype, pkv::BlockMoveArgs& a)
+{
+    if (n < 0 || block_size <= 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0)
+        return PKV_EINVAL;
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return PKV_EINVAL;
+    const int64_t esize = kv_dtype == PKV_FP8_E4M3 ? 1 : 2;
+    a.block_bytes = (int64_t)block_size * Hkv * D * esize;
+    if (a.block_bytes % 16 != 0)
+        return PKV_EUNSUPPORTED;
+    a.n = n;
+    a.scale_count = kv_dtype == PKV_FP8_E4M3 ? Hkv : 0;
+    return PKV_OK;
+}
+
+static bool moves_aligned(const void* a, const void* b, const void* c, const void* d)
+{
+    return aligned(a, 16) && aligned(b, 16) && aligned(c, 16) && aligned(d, 16);
+}
+
+int paged_kv_gather_blocks(const void* k_cache, const void* v_cache, const float* k_scale,
+                           const float* v_scale, const int32_t* block_ids, int32_t n,
+                           int32_t block_size, int32_t Hkv, int32_t D, int32_t num_blocks,
+                           int32_t kv_dtype, void* k_out, void* v_out, float* k_scale_out,
+                           float* v_scale_out, void* stream)
+{
+    pkv::BlockMoveArgs a = {};
+    int st = move_checks(n, block_size, Hkv, D, num_blocks, kv_dtype, a);
+    if (st != PKV_OK || n == 0)
+        return st;
+    if (!k_cache || !v_cache || !block_ids || !k_out || !v_out)
+        return PKV_EINVAL;
+    if (!moves_aligned(k_cache, v_cache, k_out, v_out))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale || !k_scale_out || !v_scale_out))
+        return PKV_EINVAL;
+    a.src_k = (const unsigned char*)k_cache;
+    a.src_v = (const unsigned char*)v_cache;
+    a.dst_k = (unsigned char*)k_out;
+    a.dst_v = (unsigned char*)v_out;
+    a.src_ks = k_scale;
+    a.src_vs = v_scale;
+    a.dst_ks = k_scale_out;
+    a.dst_vs = v_scale_out;
+    a.src_ids = block_ids;
+    a.dst_ids = nullptr;
+    return launched(pkv::launch_move_blocks(a, (hipStream_t)stream));
+}
+
+int paged_kv_scatter_blocks(const void* k_in, const void* v_in, const float* k_scale_in,
+                            const float* v_scale_in, const int32_t* block_ids, int32_t n,
+                            int32_t block_size, int32_t Hkv, int32_t D, int32_t num_blocks,
+                            int32_t kv_dtype, void* k_cache, void* v_cache, float* k_scale,
+                            float* v_scale, void* stream)
+{
+    pkv::BlockMoveArgs a = {};
+    int st = move_checks(n, block_size, Hkv, D, num_blocks, kv_dtype, a);
+    if (st != PKV_OK || n == 0)
+        return st;
+    if (!k_in || !v_in || !block_ids || !k_cache || !v_cache)
+        return PKV_EINVAL;
+    if (!moves_aligned(k_in, v_in, k_cache, v_cache))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale || !k_scale_in || !v_scale_in))
+        return PKV_EINVAL;
+    a.src_k = (const unsigned char*)k_in;
+    a.src_v = (const unsigned char*)v_in;
+    a.dst_k = (unsigned char*)k_cache;
+    a.dst_v = (unsigned char*)v_cache;
+    a.src_ks = k_scale_in;
+    a.src_vs = v_scale_in;
+    a.dst_ks = k_scale;
+    a.dst_vs = v_scale;
+    a.src_ids = nullptr;
+    a.dst_ids = block_ids;
+    return launched(pkv::launch_move_blocks(a, (hipStream_t)stream));
+}
+
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                         int32_t block_size, int32_t Hkv, int32_t D, int32_t num_blocks,
+                         int32_t kv_dtype, void* stream)
+{
+    pkv::BlockMoveArgs a = {};
+    int st = move_checks(n, block_size, Hkv, D, num_blocks, kv_dtype, a);
+    if (st != PKV_OK || n == 0)
+        return st;
+    if (!k_cache || !v_cache || !src_ids || !dst_ids)
+        return PKV_EINVAL;
+    if (!moves_aligned(k_cache, v_cache, k_cache, v_cache))
+        return PKV_EINVAL;
+    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    a.src_k = (const unsigned char*)k_cache;
+    a.src_v = (const unsigned char*)v_cache;
+    a.dst_k = (unsigned char*)k_cache;
+    a.dst_v = (unsigned char*)v_cache;
+    a.src_ks = k_scale;
+    a.src_vs = v_scale;
+    a.dst_ks = k_scale;
+    a.dst_vs = v_scale;
+    a.src_ids = src_ids;
+    a.dst_ids = dst_ids;
+    return launched(pkv::launch_move_blocks(a, (hipStream_t)stream));
+}
+
 int split_context_reduce(const float* partial_out, const float* partial_lse,
                          const int32_t* context_lens, int32_t B, int32_t Hq, int32_t D,
                          int32_t split_tokens, int32_t max_splits, float* out, float* lse_out,

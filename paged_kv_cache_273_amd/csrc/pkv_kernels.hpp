@@ -73,6 +73,24 @@ struct WriteArgs {
     int32_t max_blocks, B, max_query_len, Hkv, D, block_size, kv_dtype;
 };
 
+// Whole-block moves: destination block dst_ids[i] (i if null) of the
+// destination pools takes source block src_ids[i] (i if null).
+struct BlockMoveArgs {
+    const unsigned char* src_k;
+    const unsigned char* src_v;
+    unsigned char* dst_k;
+    unsigned char* dst_v;
+    const float* src_ks;      // fp8 scales [.., scale_count], or null
+    const float* src_vs;
+    float* dst_ks;
+    float* dst_vs;
+    const int32_t* src_ids;
+    const int32_t* dst_ids;
+    long long block_bytes;    // bytes of one K (or V) block, a multiple of 16
+    int32_t n;                // blocks to move
+    int32_t scale_count;      // scales per block (Hkv) when fp8, else 0
+};
+
 struct ReduceArgs {
     const float* partial_out;
     const float* partial_lse;
@@ -90,6 +108,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, int D,
                                   int block_size, int kv_dtype, bool nt, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_move_blocks(const BlockMoveArgs& a, hipStream_t stream);
 // Causal attention of several new tokens per sequence on the balanced
 // schedule; nct = 16-column MFMA tiles per wave (1 or 2).
 hipError_t launch_multiquery(const DecodeArgs& a, const BalanceArgs& ws, int D, int block_size,

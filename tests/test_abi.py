@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                             "split_context_reduce", "paged_decode_attention_balanced",
                             "paged_decode_workspace_size", "paged_kv_write",
                             "paged_multiquery_attention", "paged_multiquery_workspace_size",
-                            "pkv_status_string"]), names
+                            "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
+                            "paged_kv_copy_blocks", "pkv_status_string"]), names
 
 
 def test_block_manager_header_declares_its_calls():
@@ -236,3 +237,22 @@ def test_multiquery_workspace_size_rejects(pkv):
     assert L.paged_multiquery_workspace_size(8, 2, 64, 8, 0, 4) == -2
     assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 7, 4) == -1
     assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 0, -1) == -1
+
+
+def test_block_moves_reject(pkv):
+    L = pkv.lib()
+    f = 0x1000
+    g = L.paged_kv_gather_blocks
+    # k, v, ks, vs, ids, n, bs, Hkv, D, nb, dt, ko, vo, kso, vso, stream
+    assert g(f, f, None, None, f, -1, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
+    assert g(f, f, None, None, None, 4, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
+    assert g(f, f, None, None, f, 4, 16, 2, 64, 8, 1, f, f, None, None, None) == -1   # fp8, no scales
+    assert g(f, f, None, None, f, 4, 1, 1, 7, 8, 1, f, f, f, f, None) == -2          # 7-byte blocks
+    assert g(0x1008, f, None, None, f, 4, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
+    assert g(f, f, None, None, f, 0, 16, 2, 64, 8, 0, f, f, None, None, None) == 0
+    s = L.paged_kv_scatter_blocks
+    assert s(f, f, None, None, f, 4, 16, 2, 64, 0, 0, f, f, None, None, None) == -1  # no blocks
+    assert s(f, f, None, None, f, 4, 16, 2, 64, 8, 3, f, f, None, None, None) == -1  # dtype
+    c = L.paged_kv_copy_blocks
+    assert c(f, f, None, None, f, None, 2, 16, 2, 64, 8, 0, None) == -1
+    assert c(f, f, None, None, f, f, 0, 16, 2, 64, 8, 0, None) == 0
