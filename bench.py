@@ -42,11 +42,16 @@ def _args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--mode", default="auto",
-                   choices=["auto", "balanced", "split", "single", "multiquery"],
+                   choices=["auto", "balanced", "split", "single", "multiquery", "swap",
+                            "blockmanager"],
                    help="attention schedule: work-balanced, fixed splits + reduce, or one "
                         "wave per (sequence, kv head); auto = the workload's own split size "
                         "if it has one, multiquery if it has several new tokens per "
-                        "sequence, else balanced")
+                        "sequence, else balanced; swap = whole-block moves of preempted "
+                        "sequences to pinned host memory and back; blockmanager = host cost "
+                        "of the C++ block manager on a serving trace")
+    p.add_argument("--preempt", type=int, default=8,
+                   help="sequences swapped out and back in (--mode swap)")
     p.add_argument("--split", type=int, default=None, help="split_tokens for --mode split")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
@@ -72,6 +77,10 @@ def main():
     from synthetic import generate, generate_multiquery, make_workload
 
     wl = make_workload(a.workload)
+    if a.mode == "swap":
+        return _bench_swap(a, wl)
+    if a.mode == "blockmanager":
+        return _bench_block_manager(a)
     multi = wl.q_uniform != (1, 1)
     mode = a.mode
     if mode == "auto":
@@ -242,6 +251,183 @@ def main():
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": per_layer,
         },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+HOST_LINK_GBS = 64.0     # PCIe 5.0 x16, one direction
+
+
+def _bench_swap(a, wl):
+    """Preemption by swapping ([C] "When the cache fills"): the blocks of
+    --preempt sequences are gathered into pinned host memory and scattered
+    back into freshly chosen blocks of the pool; and the same gather into
+    device memory (the HBM-bound form used for copy-on-write)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_273_amd as pkv
+    from synthetic import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate(wl, groups=[])
+    nb = inp.num_blocks
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    k = torch.randn((nb, wl.block_size, wl.Hkv, wl.D), device=dev, generator=g).to(
+        torch.bfloat16).view(torch.int16)
+    v = torch.randn((nb, wl.block_size, wl.Hkv, wl.D), device=dev, generator=g).to(
+        torch.bfloat16).view(torch.int16)
+    P = min(a.preempt, wl.B)
+    nblk = (inp.context_lens[:P].astype(np.int64) + wl.block_size - 1) // wl.block_size
+    ids = np.concatenate([inp.block_tables[b, :nblk[b]] for b in range(P)]).astype(np.int32)
+    n = ids.size
+    block_bytes = wl.block_size * wl.Hkv * wl.D * 2
+    moved = 2 * n * block_bytes                                  # K and V
+    ids_d = torch.from_numpy(ids).to(dev)
+    back = torch.from_numpy(np.random.default_rng(2).permutation(ids)).to(dev)
+    host_k = torch.empty((n,) + k.shape[1:], dtype=k.dtype).pin_memory()
+    host_v = torch.empty_like(host_k).pin_memory()
+    dev_k = torch.empty((n,) + k.shape[1:], dtype=k.dtype, device=dev)
+    dev_v = torch.empty_like(dev_k)
+
+    def timed(fn):
+        for _ in range(max(1, a.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / a.steps
+
+    t_out = timed(lambda: pkv.paged_kv_gather_blocks(k, v, ids_d, host_k, host_v))
+    t_in = timed(lambda: pkv.paged_kv_scatter_blocks(host_k, host_v, back, k, v))
+    t_dev = timed(lambda: pkv.paged_kv_gather_blocks(k, v, ids_d, dev_k, dev_v))
+    out_gbs, in_gbs = moved / t_out / 1e9, moved / t_in / 1e9
+    dev_gbs = 2 * moved / t_dev / 1e9                           # read + write of HBM
+    res = {
+        "metric": "KV swap GB/s (blocks of preempted sequences, device <-> pinned host)",
+        "value": round(moved * 2 / (t_out + t_in) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round((t_out + t_in) * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "preempted_sequences": P, "blocks": n,
+                   "block_bytes": block_bytes, "bytes_each_way": moved,
+                   "step": "paged_kv_gather_blocks to pinned host + paged_kv_scatter_blocks "
+                           "back into permuted blocks"},
+        "swap_out_gbs": round(out_gbs, 2), "swap_in_gbs": round(in_gbs, 2),
+        "roofline": {"bound": "host link", "kernel": "move_blocks_kernel (device <-> host)",
+                     "achieved": round(max(out_gbs, in_gbs), 2), "peak": HOST_LINK_GBS,
+                     "unit": "GB/s", "frac": round(max(out_gbs, in_gbs) / HOST_LINK_GBS, 4),
+                     "traffic": None},
+        "device_gather": {"bound": "hbm", "achieved": round(dev_gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(dev_gbs / HBM_PEAK_GBS, 4),
+                          "launch_us": round(t_dev * 1e6, 2),
+                          "algorithmic_bytes_per_launch": 2 * moved},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _serving_trace(seed, n_requests, prompt_system, user_len, decode_steps, batch):
+    """A seeded request stream in the shape of [B] "Prefix Caching": most
+    requests open with one of a few 500-token system prompts."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    systems = [list(rng.integers(0, 32000, prompt_system)) for _ in range(4)]
+    reqs = []
+    for r in range(n_requests):
+        sysp = systems[rng.integers(0, 4)] if rng.random() < 0.8 else \
+            list(rng.integers(0, 32000, prompt_system))
+        user = list(rng.integers(0, 32000, int(rng.integers(user_len // 2, user_len * 2))))
+        gen = [int(x) for x in rng.integers(0, 32000, decode_steps)]
+        reqs.append((np.asarray(sysp + user, dtype=np.int32), gen))
+    return reqs
+
+
+def _run_trace(mgr_add, mgr_append, mgr_release, mgr_export, reqs, batch):
+    """Continuous batching ([B] "Continuous Batching"): up to `batch` live
+    sequences; each iteration appends one token to each, exports the
+    tables, retires finished ones and admits waiting ones."""
+    live, nxt, cached, prompt = {}, 0, 0, 0
+    steps = 0
+    while nxt < len(reqs) or live:
+        while len(live) < batch and nxt < len(reqs):
+            toks, gen = reqs[nxt]
+            cached += mgr_add(nxt, toks)
+            prompt += len(toks)
+            live[nxt] = list(gen)
+            nxt += 1
+        seqs = list(live)
+        mgr_append(seqs, [live[s].pop() for s in seqs])
+        mgr_export(seqs)
+        steps += 1
+        for s in [s for s, g in live.items() if not g]:
+            mgr_release(s)
+            del live[s]
+    return steps, cached, prompt
+
+
+def _bench_block_manager(a):
+    """Host cost of the C++ block manager on a serving trace (admission with
+    prefix lookup, one append per live sequence per step, table export),
+    and the same trace through the Python reference model."""
+    import numpy as np
+
+    from paged_kv_cache_273_amd.block_manager import BlockManager
+
+    bs, nb, batch, width = 16, 65536, 64, 128
+    reqs = _serving_trace(273, 512, 500, 200, 64, batch)
+    bm = BlockManager(nb, bs)
+
+    def append_all(seqs, toks):          # one token per live sequence, one call
+        bm.append_batch(seqs, np.arange(len(seqs) + 1, dtype=np.int32), toks)
+
+    t0 = time.perf_counter()
+    steps, cached, prompt = _run_trace(bm.add, append_all, bm.release,
+                                       lambda seqs: bm.export(seqs, width), reqs, batch)
+    el = time.perf_counter() - t0
+    st = bm.stats()
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle.block_manager as ref
+
+        m = ref.RefBlockManager(nb, bs)
+
+        def export(seqs):
+            return [m.table(s) for s in seqs]
+
+        def ref_append(seqs, toks):
+            for s_, t_ in zip(seqs, toks):
+                m.append(s_, [t_])
+
+        sub = reqs[:96]
+        t1 = time.perf_counter()
+        rsteps, _, _ = _run_trace(m.add, ref_append, m.release, export, sub, batch)
+        rel = time.perf_counter() - t1
+        cpu = {"value": round(rel / rsteps * 1e6, 1), "unit": "us per step", "cores": 1,
+               "kind": "oracle",
+               "sample": f"first 96 of 512 requests ({rsteps} steps), Python reference model"}
+    res = {
+        "metric": "host block-manager us per decode step (64 live sequences, prefix cache)",
+        "value": round(el / steps * 1e6, 2), "unit": "us per step", "n_gpus": 1,
+        "steps": steps, "warmup": 0, "ms_per_step": round(el / steps * 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": "serving trace: 512 requests, 80% open with one of 4 "
+                               "500-token system prompts, user 100-400 tokens, 64 decode "
+                               "tokens, batch 64, block 16, 65536 blocks",
+                   "prompt_tokens": prompt, "cached_prompt_tokens": cached,
+                   "prefix_hit_rate": round(cached / prompt, 4),
+                   "prompt_block_hits": st["prompt_block_hits"],
+                   "prompt_block_lookups": st["prompt_block_lookups"]},
+        "total_host_seconds": round(el, 4),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

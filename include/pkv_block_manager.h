@@ -81,6 +81,13 @@ int pkv_bm_add(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int32_
 /* Extends `seq` by tokens[0, n) (one decode step, or a chunk), n >= 0. */
 int pkv_bm_append(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t n);
 
+/* One call per step: appends tokens[token_start[i], token_start[i+1]) to
+ * seqs[i] for i = 0, 1, ... in order, as pkv_bm_append would, stopping at
+ * the first sequence that fails.  Returns the number of sequences extended
+ * (n_seqs on full success); if the first one fails, its negative status. */
+int32_t pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seqs, int32_t n_seqs,
+                            const int32_t* token_start, const int32_t* tokens);
+
 /* `child` starts as a copy of `parent` sharing all of its blocks. */
 int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
 

@@ -34,7 +34,8 @@ EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "pkv_status_string", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
            "paged_kv_copy_blocks",
            # host block manager (include/pkv_block_manager.h; binding in block_manager.py)
-           "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append", "pkv_bm_fork",
+           "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append",
+           "pkv_bm_append_batch", "pkv_bm_fork",
            "pkv_bm_release", "pkv_bm_take_copies", "pkv_bm_context_len", "pkv_bm_table",
            "pkv_bm_export", "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru")
 

@@ -36,6 +36,8 @@ def _setup(L):
     L.pkv_bm_add.argtypes = [_P, _I64, _P, _I32, _P]
     L.pkv_bm_append.restype = C.c_int
     L.pkv_bm_append.argtypes = [_P, _I64, _P, _I32]
+    L.pkv_bm_append_batch.restype = _I32
+    L.pkv_bm_append_batch.argtypes = [_P, _P, _I32, _P, _P]
     L.pkv_bm_fork.restype = C.c_int
     L.pkv_bm_fork.argtypes = [_P, _I64, _I64]
     L.pkv_bm_release.restype = C.c_int
@@ -102,6 +104,18 @@ class BlockManager:
         t = _i32(tokens)
         _check("pkv_bm_append", self._L.pkv_bm_append(self._h, int(seq), t.ctypes.data if t.size
                                                       else None, t.size))
+
+    def append_batch(self, seqs, token_start, tokens) -> int:
+        """Appends tokens[token_start[i]:token_start[i+1]] to seqs[i] in order,
+        stopping at the first failure; returns how many sequences were
+        extended (raises if the first one fails)."""
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        ts, t = _i32(token_start), _i32(tokens)
+        if ts.size != s.size + 1:
+            raise ValueError("token_start must hold len(seqs) + 1 offsets")
+        return _check("pkv_bm_append_batch",
+                      self._L.pkv_bm_append_batch(self._h, s.ctypes.data, s.size, ts.ctypes.data,
+                                                  t.ctypes.data if t.size else ts.ctypes.data))
 
     def fork(self, parent: int, child: int) -> None:
         _check("pkv_bm_fork", self._L.pkv_bm_fork(self._h, int(parent), int(child)))

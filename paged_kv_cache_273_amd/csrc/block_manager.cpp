@@ -285,6 +285,28 @@ int pkv_bm_append(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int
     }
 }
 
+int32_t pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seqs, int32_t n_seqs,
+                            const int32_t* token_start, const int32_t* tokens)
+{
+    if (!bm || n_seqs < 0 || (n_seqs > 0 && (!seqs || !token_start || !tokens)))
+        return PKV_EINVAL;
+    std::lock_guard<std::mutex> g(bm->mu);
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        const int32_t n = token_start[i + 1] - token_start[i];
+        if (n < 0)
+            return i;
+        int st;
+        try {
+            st = bm->append(seqs[i], tokens + token_start[i], n);
+        } catch (const std::bad_alloc&) {
+            st = PKV_ENOMEM;
+        }
+        if (st != PKV_OK)
+            return i == 0 ? st : i;
+    }
+    return n_seqs;
+}
+
 int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child)
 {
     if (!bm)

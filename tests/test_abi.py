@@ -45,6 +45,7 @@ def test_header_declares_the_boundary():
 def test_block_manager_header_declares_its_calls():
     names = _declared(HEADERS[1:])
     assert names == sorted(["pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append",
+                            "pkv_bm_append_batch",
                             "pkv_bm_fork", "pkv_bm_release", "pkv_bm_take_copies",
                             "pkv_bm_context_len", "pkv_bm_table", "pkv_bm_export",
                             "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru"]), names

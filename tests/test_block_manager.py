@@ -200,3 +200,34 @@ def test_namespace_changes_keys_not_behaviour(bmmod):
         assert m.add(1, list(range(13))) == 12
         assert m.table(0)[:3] == m.table(1)[:3]
     assert a.table(1) == b.table(1)
+
+
+def test_append_batch_equals_appends_in_order(bmmod):
+    """The batched call behaves as pkv_bm_append per sequence in order,
+    stopping at the first sequence that cannot get its blocks."""
+    rng = random.Random(5)
+    a, ref = bmmod.BlockManager(14, 4), RefBlockManager(14, 4)
+    for s in range(4):
+        toks = [rng.randrange(50) for _ in range(5 + s)]
+        assert a.add(s, toks) == ref.add(s, toks)
+    a.fork(1, 9)
+    ref.fork(1, 9)
+    for it in range(6):
+        seqs = [0, 9, 1, 2, 3]
+        toks = [[rng.randrange(50) for _ in range(rng.randrange(0, 4))] for _ in seqs]
+        start = np.cumsum([0] + [len(t) for t in toks])
+        flat = [x for t in toks for x in t]
+        done = 0
+        try:
+            for s, t in zip(seqs, toks):
+                ref.append(s, t)
+                done += 1
+        except RefNoSpace:
+            pass
+        if done == 0 and any(len(t) for t in toks[:1]):
+            with pytest.raises(bmmod.NoSpace):
+                a.append_batch(seqs, start, flat)
+        else:
+            assert a.append_batch(seqs, start, flat) == done
+        assert a.take_copies() == ref.take_copies()
+        _same_state(a, ref)
