@@ -64,6 +64,12 @@ def lib():
         "orc_split_reduce": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
         "orc_fp8_block_scales": (None, [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
         "orc_fp8_quantize_pool": (None, [_P, _P, _I32, _I32, _I32, _I32, _P]),
+        "orc_int8_quantize": (C.c_uint8, [C.c_uint16, _F32, _F32]),
+        "orc_fp8_wide_scales": (None, [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                       _P]),
+        "orc_int8_block_params": (None, [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                         _P]),
+        "orc_quantize_pool": (None, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
         "orc_gather_blocks": (None, [_P, _P, _I32, _I64, _P]),
         "orc_scatter_blocks": (None, [_P, _P, _I32, _I64, _P]),
         "orc_copy_blocks": (None, [_P, _P, _P, _I32, _I64]),
@@ -87,7 +93,8 @@ def _ptr(a):
     return a.ctypes.data
 
 
-_DT = {"bf16": 0, "fp8": 1, 0: 0, 1: 1}
+_DT = {"bf16": 0, "fp8": 1, "fp8_head": 2, "fp8_tensor": 3, "int8": 4,
+       0: 0, 1: 1, 2: 2, 3: 3, 4: 4}
 
 
 # ---------------------------------------------------------------- sizes
@@ -278,3 +285,38 @@ def copy_blocks(pool, src, dst):
     src = np.ascontiguousarray(src, dtype=np.int32)
     dst = np.ascontiguousarray(dst, dtype=np.int32)
     lib().orc_copy_blocks(_ptr(pool), _ptr(src), _ptr(dst), src.size, _block_bytes(pool))
+
+
+# ---------------------------------------------------------------- other 1-byte formats
+def int8_quantize(x_bf16: int, scale: float, zero_point: float) -> int:
+    return int(lib().orc_int8_quantize(int(x_bf16), float(scale), float(zero_point)))
+
+
+def fp8_wide_scales(src_bf16, block_tables, context_lens, block_size, per_tensor=False):
+    """E4M3 scales per kv head ([Hkv]) or per tensor ([1])."""
+    nb, _, Hkv, D = src_bf16.shape
+    out = np.empty(1 if per_tensor else Hkv, dtype=np.float32)
+    lib().orc_fp8_wide_scales(_ptr(src_bf16), _ptr(block_tables), block_tables.shape[1],
+                              _ptr(context_lens), context_lens.shape[0], Hkv, D, block_size,
+                              nb, int(bool(per_tensor)), _ptr(out))
+    return out
+
+
+def int8_block_params(src_bf16, block_tables, context_lens, block_size, symmetric=False):
+    """[num_blocks, Hkv, 2] (scale, zero point) pairs."""
+    nb, _, Hkv, D = src_bf16.shape
+    out = np.empty((nb, Hkv, 2), dtype=np.float32)
+    lib().orc_int8_block_params(_ptr(src_bf16), _ptr(block_tables), block_tables.shape[1],
+                                _ptr(context_lens), context_lens.shape[0], Hkv, D, block_size,
+                                nb, int(bool(symmetric)), _ptr(out))
+    return out
+
+
+def quantize_pool(src_bf16, scales, kv_dtype):
+    """A bf16 pool quantised to 1-byte codes of kv_dtype ("fp8", "fp8_head",
+    "fp8_tensor", "int8")."""
+    nb, bs, Hkv, D = src_bf16.shape
+    out = np.empty(src_bf16.shape, dtype=np.uint8)
+    lib().orc_quantize_pool(_ptr(src_bf16), _ptr(np.ascontiguousarray(scales, np.float32)),
+                            _DT[kv_dtype], nb, bs, Hkv, D, _ptr(out))
+    return out

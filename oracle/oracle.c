@@ -153,6 +153,29 @@ uint8_t orc_e4m3_quantize(uint16_t x_bf16, float scale)
 }
 
 /* ------------------------------------------------------------------ */
+/* INT8 cache ([B] "INT8 KV cache": symmetric or asymmetric integer     */
+/* quantisation with a scale and a zero point).  Codes are unsigned     */
+/* bytes u in [0, 255] standing for scale * (u - zero_point); symmetric */
+/* quantisation is zero_point = 128.  Encoding: y = x / scale as one    */
+/* binary32 division, rounded to the nearest integer (ties to even),    */
+/* plus the zero point, clamped to [0, 255]; NaN gives code 0.          */
+/* ------------------------------------------------------------------ */
+uint8_t orc_int8_quantize(uint16_t x_bf16, float scale, float zero_point)
+{
+    float x = (float)orc_bf16_value(x_bf16);
+    float y = x / scale;
+    double v;
+    if (y != y)
+        return 0;
+    v = (double)rintf(y) + (double)zero_point;
+    if (v < 0.0)
+        v = 0.0;
+    if (v > 255.0)
+        v = 255.0;
+    return (uint8_t)v;
+}
+
+/* ------------------------------------------------------------------ */
 /* Paged addressing                                                   */
 /* [B] "PagedAttention": logical block j of a sequence lives in the    */
 /* physical block its block table names; a token at logical position t */
@@ -165,18 +188,58 @@ static int64_t pool_index(int32_t phys, int32_t slot, int32_t h, int32_t d,
     return (((int64_t)phys * bs + slot) * Hkv + h) * D + d;
 }
 
-/* Dequantised (or widened) cache element.  kv_dtype 0 = bf16 bits,
- * 1 = E4M3FN codes with a per-(physical block, kv head) binary32 scale
- * ([B] "FP8 KV cache": dequantise on read). */
+/* Cache formats (kv_dtype) and where an element's scale lives
+ * ([B] "FP8 KV cache": a per-tensor or per-head scale; the per-(block,
+ * head) scale is the finest of these; [B] "INT8 KV cache"):
+ *   0  bf16 bits, no scale
+ *   1  E4M3FN codes, scales[phys * Hkv + h]
+ *   2  E4M3FN codes, scales[h]            (per kv head)
+ *   3  E4M3FN codes, scales[0]            (per tensor)
+ *   4  uint8 codes, (scale, zero point) = scales[2 (phys * Hkv + h)], [.. + 1] */
+static int orc_valid_dtype(int32_t kv_dtype)
+{
+    return kv_dtype >= 0 && kv_dtype <= 4;
+}
+
+static int64_t scale_index(int32_t kv_dtype, int32_t phys, int32_t h, int32_t Hkv)
+{
+    switch (kv_dtype) {
+    case 1: return (int64_t)phys * Hkv + h;
+    case 2: return h;
+    case 3: return 0;
+    default: return 2 * ((int64_t)phys * Hkv + h);
+    }
+}
+
+/* Dequantised (or widened) cache element (dequantise on read). */
 static double cache_value(const void* cache, const float* scales, int32_t kv_dtype,
                           int32_t phys, int32_t slot, int32_t h, int32_t d,
                           int32_t bs, int32_t Hkv, int32_t D)
 {
     int64_t i = pool_index(phys, slot, h, d, bs, Hkv, D);
+    int64_t si;
     if (kv_dtype == 0)
         return orc_bf16_value(((const uint16_t*)cache)[i]);
-    return orc_e4m3_value(((const uint8_t*)cache)[i])
-           * (double)scales[(int64_t)phys * Hkv + h];
+    si = scale_index(kv_dtype, phys, h, Hkv);
+    if (kv_dtype == 4)
+        return (double)scales[si] * ((double)((const uint8_t*)cache)[i] - (double)scales[si + 1]);
+    return orc_e4m3_value(((const uint8_t*)cache)[i]) * (double)scales[si];
+}
+
+/* Stores one bf16 value into a cache element of any format. */
+static void store_value(void* cache, const float* scales, int32_t kv_dtype, int64_t dst,
+                        uint16_t x, int32_t phys, int32_t h, int32_t Hkv)
+{
+    int64_t si;
+    if (kv_dtype == 0) {
+        ((uint16_t*)cache)[dst] = x;
+        return;
+    }
+    si = scale_index(kv_dtype, phys, h, Hkv);
+    if (kv_dtype == 4)
+        ((uint8_t*)cache)[dst] = orc_int8_quantize(x, scales[si], scales[si + 1]);
+    else
+        ((uint8_t*)cache)[dst] = orc_e4m3_quantize(x, scales[si]);
 }
 
 /* Checks the preconditions a block table must meet before any kernel
@@ -230,15 +293,8 @@ void orc_append(const uint16_t* k_new, const uint16_t* v_new,
             for (d = 0; d < D; ++d) {
                 int64_t src = ((int64_t)b * Hkv + h) * D + d;
                 int64_t dst = pool_index(phys, slot, h, d, block_size, Hkv, D);
-                if (kv_dtype == 0) {
-                    ((uint16_t*)k_cache)[dst] = k_new[src];
-                    ((uint16_t*)v_cache)[dst] = v_new[src];
-                } else {
-                    float ks = k_scale[(int64_t)phys * Hkv + h];
-                    float vs = v_scale[(int64_t)phys * Hkv + h];
-                    ((uint8_t*)k_cache)[dst] = orc_e4m3_quantize(k_new[src], ks);
-                    ((uint8_t*)v_cache)[dst] = orc_e4m3_quantize(v_new[src], vs);
-                }
+                store_value(k_cache, k_scale, kv_dtype, dst, k_new[src], phys, h, Hkv);
+                store_value(v_cache, v_scale, kv_dtype, dst, v_new[src], phys, h, Hkv);
             }
         }
     }
@@ -369,7 +425,7 @@ int32_t orc_paged_attention(const uint16_t* query, const void* k_cache, const vo
 {
     int32_t b, hq;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || block_size <= 0
-        || split_tokens < 0 || (kv_dtype != 0 && kv_dtype != 1))
+        || split_tokens < 0 || !orc_valid_dtype(kv_dtype))
         return -1;
     for (b = 0; b < B; ++b) {
         int32_t T = context_lens[b];
@@ -493,15 +549,8 @@ int32_t orc_write_tokens(const uint16_t* k_rows, const uint16_t* v_rows,
                 for (d = 0; d < D; ++d) {
                     int64_t src = (row * Hkv + h) * D + d;
                     int64_t dst = pool_index(phys, slot, h, d, block_size, Hkv, D);
-                    if (kv_dtype == 0) {
-                        ((uint16_t*)k_cache)[dst] = k_rows[src];
-                        ((uint16_t*)v_cache)[dst] = v_rows[src];
-                    } else {
-                        ((uint8_t*)k_cache)[dst] =
-                            orc_e4m3_quantize(k_rows[src], k_scale[(int64_t)phys * Hkv + h]);
-                        ((uint8_t*)v_cache)[dst] =
-                            orc_e4m3_quantize(v_rows[src], v_scale[(int64_t)phys * Hkv + h]);
-                    }
+                    store_value(k_cache, k_scale, kv_dtype, dst, k_rows[src], phys, h, Hkv);
+                    store_value(v_cache, v_scale, kv_dtype, dst, v_rows[src], phys, h, Hkv);
                 }
         }
     }
@@ -524,7 +573,7 @@ int32_t orc_multiquery_attention(const uint16_t* query, const int32_t* query_sta
 {
     int32_t b, i, hq;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || block_size <= 0
-        || (kv_dtype != 0 && kv_dtype != 1))
+        || !orc_valid_dtype(kv_dtype))
         return -1;
     for (b = 0; b < B; ++b) {
         int32_t T = context_lens[b];
@@ -630,6 +679,127 @@ void orc_fp8_block_scales(const uint16_t* src_bf16, const int32_t* block_tables,
         }
     }
     free(live);
+}
+
+/* Live slots of every physical block (the largest count any table gives
+ * it); caller frees. */
+static int32_t* live_slots(const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t B, int32_t block_size,
+                           int32_t num_blocks)
+{
+    int32_t* live = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t));
+    int32_t b, j;
+    for (b = 0; b < B; ++b) {
+        int32_t T = context_lens[b];
+        int32_t nblk = (T + block_size - 1) / block_size;
+        for (j = 0; j < nblk; ++j) {
+            int32_t n = T - j * block_size;
+            int32_t p = block_tables[(int64_t)b * max_blocks + j];
+            if (n > block_size)
+                n = block_size;
+            if (n > live[p])
+                live[p] = n;
+        }
+    }
+    return live;
+}
+
+/* Per-kv-head (per_tensor = 0) or per-tensor (per_tensor = 1) E4M3 scales:
+ * amax / 448 over the live tokens of every block (1 if amax = 0). */
+void orc_fp8_wide_scales(const uint16_t* src_bf16, const int32_t* block_tables,
+                         int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                         int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                         int32_t per_tensor, float* scales)
+{
+    int32_t* live = live_slots(block_tables, max_blocks, context_lens, B, block_size,
+                               num_blocks);
+    int32_t p, h, slot, d;
+    double amax_t = 0.0;
+    for (h = 0; h < Hkv; ++h) {
+        double amax = 0.0;
+        for (p = 0; p < num_blocks; ++p)
+            for (slot = 0; slot < live[p]; ++slot)
+                for (d = 0; d < D; ++d) {
+                    double v = fabs(orc_bf16_value(
+                        src_bf16[pool_index(p, slot, h, d, block_size, Hkv, D)]));
+                    if (v > amax)
+                        amax = v;
+                }
+        if (!per_tensor)
+            scales[h] = amax > 0.0 ? (float)amax / 448.0f : 1.0f;
+        if (amax > amax_t)
+            amax_t = amax;
+    }
+    if (per_tensor)
+        scales[0] = amax_t > 0.0 ? (float)amax_t / 448.0f : 1.0f;
+    free(live);
+}
+
+/* INT8 (scale, zero point) pairs per (block, kv head) over the block's live
+ * tokens.  Symmetric: scale = amax / 127, zero point 128.  Asymmetric:
+ * scale = (max - min) / 255, zero point = rint(-min / scale) clamped to
+ * [0, 255] (binary32 arithmetic).  A block or head with no spread gets
+ * scale 1 (symmetric: amax = 0; asymmetric: max = min). */
+void orc_int8_block_params(const uint16_t* src_bf16, const int32_t* block_tables,
+                           int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                           int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                           int32_t symmetric, float* params)
+{
+    int32_t* live = live_slots(block_tables, max_blocks, context_lens, B, block_size,
+                               num_blocks);
+    int32_t p, h, slot, d;
+    for (p = 0; p < num_blocks; ++p)
+        for (h = 0; h < Hkv; ++h) {
+            double lo = INFINITY, hi = -INFINITY, amax = 0.0;
+            float sc, zp;
+            for (slot = 0; slot < live[p]; ++slot)
+                for (d = 0; d < D; ++d) {
+                    double v = orc_bf16_value(
+                        src_bf16[pool_index(p, slot, h, d, block_size, Hkv, D)]);
+                    if (v != v)
+                        continue;
+                    if (v < lo)
+                        lo = v;
+                    if (v > hi)
+                        hi = v;
+                    if (fabs(v) > amax)
+                        amax = fabs(v);
+                }
+            if (symmetric) {
+                sc = amax > 0.0 ? (float)amax / 127.0f : 1.0f;
+                zp = 128.0f;
+            } else if (hi > lo) {
+                float r;
+                sc = ((float)hi - (float)lo) / 255.0f;
+                r = rintf(-(float)lo / sc);
+                zp = r < 0.0f ? 0.0f : (r > 255.0f ? 255.0f : r);
+            } else {
+                sc = 1.0f;
+                zp = 0.0f;
+                if (lo == lo && lo < INFINITY) {
+                    float r = rintf(-(float)lo);
+                    zp = r < 0.0f ? 0.0f : (r > 255.0f ? 255.0f : r);
+                }
+            }
+            params[2 * ((int64_t)p * Hkv + h)] = sc;
+            params[2 * ((int64_t)p * Hkv + h) + 1] = zp;
+        }
+    free(live);
+}
+
+/* Quantises a whole bf16 pool in any 1-byte format (kv_dtype 1-4). */
+void orc_quantize_pool(const uint16_t* src_bf16, const float* scales, int32_t kv_dtype,
+                       int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D,
+                       uint8_t* codes)
+{
+    int32_t p, slot, h, d;
+    for (p = 0; p < num_blocks; ++p)
+        for (slot = 0; slot < block_size; ++slot)
+            for (h = 0; h < Hkv; ++h)
+                for (d = 0; d < D; ++d) {
+                    int64_t i = pool_index(p, slot, h, d, block_size, Hkv, D);
+                    store_value(codes, scales, kv_dtype, i, src_bf16[i], p, h, Hkv);
+                }
 }
 
 /* Quantises a whole bf16 pool [num_blocks, block_size, Hkv, D] with the

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_formula.py", "tests/test_oracle_fp8.py",
         "tests/test_oracle_attention.py", "tests/test_oracle_multiquery.py",
-        "tests/test_oracle_blocks.py"]
+        "tests/test_oracle_blocks.py", "tests/test_oracle_quant.py"]
 
 # (name, original text, planted text, occurrence count expected)
 MUTANTS = [
@@ -42,16 +42,16 @@ MUTANTS = [
     ("quantise_multiplies", "float y = x / scale;", "float y = x * scale;"),
     ("no_saturation", "if (a >= 448.0)\n        return (uint8_t)(sign | 0x7E);",
      "if (a >= 448.0)\n        return (uint8_t)(sign | 0x7F);"),
-    ("fp8_scale_ignores_head", "* (double)scales[(int64_t)phys * Hkv + h];",
-     "* (double)scales[(int64_t)phys * Hkv];"),
+    ("fp8_scale_ignores_head", "case 1: return (int64_t)phys * Hkv + h;",
+     "case 1: return (int64_t)phys * Hkv;"),
     ("merge_weight_sign", "w = exp(lse_parts[s] - M);", "w = exp(M - lse_parts[s]);"),
     ("merge_empty_as_lse_zero",
      "if (lse_parts[s] == -INFINITY)\n            continue;\n        w = exp(lse_parts[s] - M);",
      "w = lse_parts[s] == -INFINITY ? exp(-M) : exp(lse_parts[s] - M);"),
     ("append_wrong_slot", "slot = t % block_size;\n        for (h = 0; h < Hkv; ++h) {",
      "slot = (t + 1) % block_size;\n        for (h = 0; h < Hkv; ++h) {"),
-    ("append_swaps_k_v", "((uint16_t*)k_cache)[dst] = k_new[src];",
-     "((uint16_t*)k_cache)[dst] = v_new[src];"),
+    ("append_swaps_k_v", "store_value(k_cache, k_scale, kv_dtype, dst, k_new[src], phys, h, Hkv);",
+     "store_value(k_cache, k_scale, kv_dtype, dst, v_new[src], phys, h, Hkv);"),
     ("block_scale_amax_over_all_slots", "for (slot = 0; slot < live[p]; ++slot)",
      "for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)"),
     ("split_range_overlaps", "int32_t t0 = s * split_tokens;",
@@ -61,14 +61,23 @@ MUTANTS = [
     ("mq_query_row_of_sequence", "const uint16_t* qrow = query + row * Hq * D;",
      "const uint16_t* qrow = query + (int64_t)b * Hq * D;"),
     ("write_rows_reversed", "int32_t t = T - q + i;", "int32_t t = T - 1 - i;"),
+    ("int8_zero_point_added", "((double)((const uint8_t*)cache)[i] - (double)scales[si + 1])",
+     "((double)((const uint8_t*)cache)[i] + (double)scales[si + 1])"),
+    ("int8_truncates", "v = (double)rintf(y) + (double)zero_point;",
+     "v = (double)truncf(y) + (double)zero_point;"),
+    ("int8_clamp_254", "if (v > 255.0)\n        v = 255.0;", "if (v > 254.0)\n        v = 254.0;"),
+    ("per_head_scale_by_block", "case 2: return h;", "case 2: return (int64_t)phys * Hkv + h;"),
+    ("per_tensor_scale_by_head", "case 3: return 0;", "case 3: return h;"),
+    ("int8_params_unpaired", "default: return 2 * ((int64_t)phys * Hkv + h);",
+     "default: return (int64_t)phys * Hkv + h;"),
     ("gather_by_position", "(const char*)pool + (int64_t)ids[i] * block_bytes",
      "(const char*)pool + (int64_t)i * block_bytes"),
     ("scatter_by_position", "memcpy((char*)pool + (int64_t)ids[i] * block_bytes,",
      "memcpy((char*)pool + (int64_t)i * block_bytes,"),
     ("copy_reversed", "memcpy((char*)pool + (int64_t)dst[i] * block_bytes,\n               (const char*)pool + (int64_t)src[i] * block_bytes",
      "memcpy((char*)pool + (int64_t)src[i] * block_bytes,\n               (const char*)pool + (int64_t)dst[i] * block_bytes"),
-    ("write_v_with_k_scale", "orc_e4m3_quantize(v_rows[src], v_scale[",
-     "orc_e4m3_quantize(v_rows[src], k_scale["),
+    ("write_v_with_k_scale", "store_value(v_cache, v_scale, kv_dtype, dst, v_rows[src]",
+     "store_value(v_cache, k_scale, kv_dtype, dst, v_rows[src]"),
 ]
 
 
