@@ -50,6 +50,11 @@ def _args():
                         "sequence, else balanced; swap = whole-block moves of preempted "
                         "sequences to pinned host memory and back; blockmanager = host cost "
                         "of the C++ block manager on a serving trace")
+    p.add_argument("--kv-format", default=None,
+                   choices=["bf16", "fp8", "fp8_head", "fp8_tensor", "int8"],
+                   help="cache format (default: the workload's own); fp8 = one scale per "
+                        "block and kv head, fp8_head / fp8_tensor = one per kv head / per "
+                        "cache, int8 = per-block asymmetric scale and zero point")
     p.add_argument("--preempt", type=int, default=8,
                    help="sequences swapped out and back in (--mode swap)")
     p.add_argument("--split", type=int, default=None, help="split_tokens for --mode split")
@@ -106,21 +111,47 @@ def main():
 
     live = torch.from_numpy(np.arange(wl.block_size)[None, :] < inp.live[:, None]).to(dev)
 
+    fmt = a.kv_format or wl.kv_dtype
+    ebytes = 2 if fmt == "bf16" else 1
+
     def quant(src):
-        # fp8 cache built on the device from the bf16 source values (input
-        # preparation only: scale = amax / 448 per block and kv head)
+        # 1-byte cache built on the device from the bf16 source values (input
+        # preparation only): fp8 scale = amax / 448 per block and kv head,
+        # per kv head or per cache; int8 = asymmetric (min, max) per block
+        # and kv head
         x = up(src).view(torch.bfloat16).float()
-        xm = torch.where(live[:, :, None, None] & torch.isfinite(x), x.abs(), torch.zeros_like(x))
-        amax = xm.amax(dim=(1, 3))
+        ok = live[:, :, None, None] & torch.isfinite(x)
+        if fmt == "int8":
+            lo = torch.where(ok, x, torch.full_like(x, float("inf"))).amin(dim=(1, 3))
+            hi = torch.where(ok, x, torch.full_like(x, float("-inf"))).amax(dim=(1, 3))
+            spread = hi > lo
+            sc = torch.where(spread, (hi - lo) / 255.0, torch.ones_like(hi))
+            zp = torch.where(spread, torch.round(-lo / sc).clamp(0, 255), torch.zeros_like(hi))
+            u = (torch.round(x / sc[:, None, :, None]) + zp[:, None, :, None]).clamp(0, 255)
+            u = torch.nan_to_num(u, nan=0.0)
+            return u.to(torch.uint8).contiguous(), torch.stack([sc, zp], -1).float().contiguous()
+        xm = torch.where(ok, x.abs(), torch.zeros_like(x))
+        if fmt == "fp8":
+            amax = xm.amax(dim=(1, 3))
+        elif fmt == "fp8_head":
+            amax = xm.amax(dim=(0, 1, 3))
+        else:
+            amax = xm.amax().reshape(1)
         sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
-        y = (x / sc[:, None, :, None]).clamp(-448, 448)
+        if fmt == "fp8":
+            y = x / sc[:, None, :, None]
+        elif fmt == "fp8_head":
+            y = x / sc[None, None, :, None]
+        else:
+            y = x / sc
+        y = y.clamp(-448, 448)
         return y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc.contiguous()
 
     # one cache per layer group ([A] cross-layer KV sharing: layer l reads
     # group l // layers_per_group); bf16 workloads have a single group
     caches = []
     for g in range(wl.groups):
-        if wl.kv_dtype == "fp8":
+        if fmt != "bf16":
             k, ks = quant(inp.k_pool[g])
             v, vs = quant(inp.v_pool[g])
         else:
@@ -136,7 +167,7 @@ def main():
         max_q = int(mq.query_lens.max())
     bt, cl = up(inp.block_tables), up(inp.context_lens)
     ctx = inp.context_lens.astype(np.int64)
-    per_layer = 2 * int(ctx.sum()) * wl.Hkv * wl.D * wl.bytes_per_elem
+    per_layer = 2 * int(ctx.sum()) * wl.Hkv * wl.D * ebytes
     ideal = per_layer * wl.layers
     scale = float(inp.scale)
 
@@ -144,18 +175,19 @@ def main():
     out = torch.empty((rows, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     po = torch.empty((wl.B, wl.Hq, ms, wl.D), dtype=torch.float32, device=dev) if S else None
     pl = torch.empty((wl.B, wl.Hq, ms), dtype=torch.float32, device=dev) if S else None
-    ws = pkv.make_workspace(qs[0], caches[0][0]) if mode == "balanced" else None
+    ws = pkv.make_workspace(qs[0], caches[0][0], kv_dtype=fmt) if mode == "balanced" else None
     if mode == "multiquery":
-        ws = pkv.make_multiquery_workspace(qs[0], caches[0][0], max_q)
+        ws = pkv.make_multiquery_workspace(qs[0], caches[0][0], max_q, kv_dtype=fmt)
 
     ev = []  # (start, end) around each attention call in the timed region
 
     def step(record):
         for k, v, ks, vs, kn, vn in caches:
             if multi:
-                pkv.paged_kv_write(kn, vn, qstart, k, v, bt, cl, max_q, k_scale=ks, v_scale=vs)
+                pkv.paged_kv_write(kn, vn, qstart, k, v, bt, cl, max_q, k_scale=ks, v_scale=vs,
+                                   kv_dtype=fmt)
             else:
-                pkv.paged_kv_append(kn, vn, k, v, bt, cl, k_scale=ks, v_scale=vs)
+                pkv.paged_kv_append(kn, vn, k, v, bt, cl, k_scale=ks, v_scale=vs, kv_dtype=fmt)
         for layer in range(wl.layers):
             k, v, ks, vs, _, _ = caches[layer // wl.layers_per_group]
             q = qs[layer]
@@ -166,16 +198,18 @@ def main():
             if mode == "split":
                 pkv.paged_decode_attention(q, k, v, bt, cl, scale, split_tokens=S,
                                            partial_out=po, partial_lse=pl, k_scale=ks,
-                                           v_scale=vs)
+                                           v_scale=vs, kv_dtype=fmt)
             elif mode == "balanced":
                 pkv.paged_decode_attention_balanced(q, k, v, bt, cl, scale, workspace=ws,
-                                                    out=out, k_scale=ks, v_scale=vs)
+                                                    out=out, k_scale=ks, v_scale=vs,
+                                                    kv_dtype=fmt)
             elif mode == "multiquery":
                 pkv.paged_multiquery_attention(q, qstart, k, v, bt, cl, scale, max_q,
-                                               workspace=ws, out=out, k_scale=ks, v_scale=vs)
+                                               workspace=ws, out=out, k_scale=ks, v_scale=vs,
+                                               kv_dtype=fmt)
             else:
                 pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks,
-                                           v_scale=vs)
+                                           v_scale=vs, kv_dtype=fmt)
             if record:
                 e1.record()
                 ev.append((e0, e1))
@@ -202,11 +236,12 @@ def main():
     step_s = wall / a.steps
     gbs = ideal / step_s / 1e9
     kern_gbs = per_layer / kern_s / 1e9
-    traffic = _measured_traffic(a.traffic_json, f"{wl.name}:{mode}")
+    traffic = _measured_traffic(a.traffic_json, f"{wl.name}:{mode}"
+                                + (f":{fmt}" if fmt != wl.kv_dtype else ""))
 
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = _cpu_baseline(inp, wl, a.cpu_seconds, mq)
+        cpu = _cpu_baseline(inp, wl, a.cpu_seconds, mq, fmt)
 
     res = {
         "metric": METRIC,
@@ -219,14 +254,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.kv_dtype,
+        "dtype": fmt,
         "data": "synthetic",
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(wl.B / step_s, 1),
         "new_tokens_per_s": round(rows / step_s, 1),
         "config": {
             "workload": wl.name, "batch": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
-            "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
+            "block_size": wl.block_size, "kv_dtype": fmt,
             "ctx_sum": int(ctx.sum()), "ctx_mean": round(float(ctx.mean()), 1),
             "ctx_min": int(ctx.min()), "ctx_max": int(ctx.max()), "schedule": mode,
             "split_tokens": S, "num_blocks": inp.num_blocks, "ideal_kv_bytes_per_step": ideal,
@@ -452,24 +487,35 @@ def _measured_traffic(path, key):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(inp, wl, target_s, mq=None):
+def _oracle_cache(oracle, kp, vp, inp, wl, fmt):
+    """Host caches of format fmt built by the oracle's own encoder."""
+    if fmt == "bf16":
+        return kp.copy(), vp.copy(), None, None
+    args = (inp.block_tables, inp.context_lens, wl.block_size)
+    if fmt == "int8":
+        ks = oracle.int8_block_params(kp, *args)
+        vs = oracle.int8_block_params(vp, *args)
+    elif fmt == "fp8":
+        ks = oracle.fp8_block_scales(kp, *args)
+        vs = oracle.fp8_block_scales(vp, *args)
+    else:
+        ks = oracle.fp8_wide_scales(kp, *args, per_tensor=(fmt == "fp8_tensor"))
+        vs = oracle.fp8_wide_scales(vp, *args, per_tensor=(fmt == "fp8_tensor"))
+    return oracle.quantize_pool(kp, ks, fmt), oracle.quantize_pool(vp, vs, fmt), ks, vs
+
+
+def _cpu_baseline(inp, wl, target_s, mq=None, fmt="bf16"):
     """The oracle (single-threaded C, fp64) on whole sequences of the same
     workload until about target_s seconds of CPU time; GB/s on the same
     ideal-byte formula."""
     if mq is not None:
-        return _cpu_baseline_multiquery(mq, target_s)
+        return _cpu_baseline_multiquery(mq, target_s, fmt)
     import numpy as np
 
     import oracle
 
-    kp, vp = inp.k_pool[0], inp.v_pool[0]
-    kind = "bf16"
-    ks = vs = None
-    if wl.kv_dtype == "fp8":
-        ks = oracle.fp8_block_scales(kp, inp.block_tables, inp.context_lens, wl.block_size)
-        vs = oracle.fp8_block_scales(vp, inp.block_tables, inp.context_lens, wl.block_size)
-        kp, vp = oracle.fp8_quantize_pool(kp, ks), oracle.fp8_quantize_pool(vp, vs)
-        kind = "fp8"
+    kind = fmt
+    kp, vp, ks, vs = _oracle_cache(oracle, inp.k_pool[0], inp.v_pool[0], inp, wl, fmt)
     oracle.append(inp.k_new[0], inp.v_new[0], kp, vp, inp.block_tables, inp.context_lens,
                   wl.block_size, kv_dtype=kind, k_scale=ks, v_scale=vs)
     done_bytes = 0
@@ -482,7 +528,7 @@ def _cpu_baseline(inp, wl, target_s, mq=None):
                                np.ascontiguousarray(inp.context_lens[sl]), inp.scale,
                                block_size=wl.block_size, Hkv=wl.Hkv, kv_dtype=kind,
                                k_scale=ks, v_scale=vs)
-        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * wl.bytes_per_elem
+        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * (2 if fmt == "bf16" else 1)
         seqs += 1
         if time.perf_counter() - t0 >= target_s:
             break
@@ -495,22 +541,15 @@ def _cpu_baseline(inp, wl, target_s, mq=None):
             "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
 
 
-def _cpu_baseline_multiquery(mq, target_s):
-    """The multi-query oracle on whole sequences (bf16 or fp8 cache)."""
+def _cpu_baseline_multiquery(mq, target_s, fmt):
+    """The multi-query oracle on whole sequences."""
     import numpy as np
 
     import oracle
 
     wl, inp = mq.wl, mq.base
-    kp, vp = inp.k_pool[0], inp.v_pool[0]
-    kind = wl.kv_dtype
-    ks = vs = None
-    if kind == "fp8":
-        ks = oracle.fp8_block_scales(kp, inp.block_tables, inp.context_lens, wl.block_size)
-        vs = oracle.fp8_block_scales(vp, inp.block_tables, inp.context_lens, wl.block_size)
-        kp, vp = oracle.fp8_quantize_pool(kp, ks), oracle.fp8_quantize_pool(vp, vs)
-    else:
-        kp, vp = kp.copy(), vp.copy()
+    kind = fmt
+    kp, vp, ks, vs = _oracle_cache(oracle, inp.k_pool[0], inp.v_pool[0], inp, wl, fmt)
     oracle.write_tokens(mq.k_rows[0], mq.v_rows[0], mq.query_start, kp, vp, inp.block_tables,
                         inp.context_lens, wl.block_size, kv_dtype=kind, k_scale=ks, v_scale=vs)
     done_bytes = rows = seqs = 0
@@ -523,7 +562,7 @@ def _cpu_baseline_multiquery(mq, target_s):
                                     np.ascontiguousarray(inp.context_lens[b:b + 1]), inp.scale,
                                     block_size=wl.block_size, Hkv=wl.Hkv, kv_dtype=kind,
                                     k_scale=ks, v_scale=vs)
-        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * wl.bytes_per_elem
+        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * (2 if fmt == "bf16" else 1)
         rows += r1 - r0
         seqs += 1
         if time.perf_counter() - t0 >= target_s:

@@ -34,13 +34,24 @@
  * free block serves any sequence)
  * ------------------------------------------------------------------
  *  k_cache, v_cache : [num_blocks, block_size, Hkv, D]
- *      kv_dtype PKV_BF16     : uint16_t bf16 bits
- *      kv_dtype PKV_FP8_E4M3 : uint8_t OCP E4M3FN codes (max finite 448,
- *                              0x7F/0xFF NaN, no infinities)
- *  k_scale, v_scale : [num_blocks, Hkv] float, fp8 only (NULL for bf16).
- *      The value of a stored code c in block p, head h is
- *      decode(c) * scale[p, h] ([B] "FP8 KV cache": dequantise on read;
- *      one scale per block and kv head).
+ *      kv_dtype PKV_BF16        : uint16_t bf16 bits
+ *      kv_dtype PKV_FP8_E4M3*   : uint8_t OCP E4M3FN codes (max finite 448,
+ *                                 0x7F/0xFF NaN, no infinities)
+ *      kv_dtype PKV_INT8        : uint8_t codes u in [0, 255]
+ *  k_scale, v_scale (NULL for bf16), dequantise on read ([B] "FP8 KV
+ *  cache": a scale factor per tensor or per head; [B] "INT8 KV cache":
+ *  symmetric or asymmetric with a scale and a zero point):
+ *      PKV_FP8_E4M3            [num_blocks, Hkv] : decode(c) * scale[p, h]
+ *      PKV_FP8_E4M3_PER_HEAD   [Hkv]             : decode(c) * scale[h]
+ *      PKV_FP8_E4M3_PER_TENSOR [1]               : decode(c) * scale[0]
+ *      PKV_INT8                [num_blocks, Hkv, 2] (scale, zero point)
+ *                                                : scale * (u - zero point);
+ *          zero point integer-valued in [0, 255]; symmetric quantisation
+ *          is zero point 128.
+ *  Writes (append, write) encode x as E4M3FN(x / scale) (round to nearest
+ *  even, saturate to +-448) or clamp(rint(x / scale) + zero point, 0, 255)
+ *  (NaN -> 0), with a correctly rounded binary32 division; the scales are
+ *  the caller's (values outside their range saturate).
  *  block_tables : [B, max_blocks] int32.  Logical block j of sequence b
  *      lives in physical block block_tables[b, j]; token t of sequence b
  *      is slot t % block_size of logical block t / block_size
@@ -84,7 +95,11 @@ enum pkv_status {
 
 enum pkv_dtype {
     PKV_BF16 = 0,
-    PKV_FP8_E4M3 = 1        /* OCP E4M3FN, per-(block, kv head) fp32 scale */
+    PKV_FP8_E4M3 = 1,           /* OCP E4M3FN, per-(block, kv head) fp32 scale */
+    PKV_FP8_E4M3_PER_HEAD = 2,  /* OCP E4M3FN, one scale per kv head           */
+    PKV_FP8_E4M3_PER_TENSOR = 3,/* OCP E4M3FN, one scale for the whole cache    */
+    PKV_INT8 = 4                /* uint8 codes, per-(block, kv head) scale and
+                                   zero point                                   */
 };
 
 /* Supported shapes of this build: D in {64, 128}; block_size in {16, 32};

@@ -26,7 +26,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH, PKV_ENOSPACE, PKV_ENOMEM = 0, -1, -2, -3, -4, -5
-PKV_BF16, PKV_FP8_E4M3 = 0, 1
+PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E4M3_PER_HEAD, PKV_FP8_E4M3_PER_TENSOR, PKV_INT8 = 0, 1, 2, 3, 4
+KV_DTYPES = {"bf16": PKV_BF16, "fp8": PKV_FP8_E4M3, "fp8_head": PKV_FP8_E4M3_PER_HEAD,
+             "fp8_tensor": PKV_FP8_E4M3_PER_TENSOR, "int8": PKV_INT8}
 
 EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "paged_decode_attention_balanced", "paged_decode_workspace_size",
@@ -110,7 +112,16 @@ _BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
 _FP8_CODES = (torch.uint8, torch.float8_e4m3fn)
 
 
-def _kv_dtype(cache: torch.Tensor) -> int:
+def _kv_dtype(cache: torch.Tensor, kv_dtype=None) -> int:
+    """The cache format: given (a pkv_dtype code or a name of KV_DTYPES), or
+    inferred from the tensor (bf16 bits, or E4M3FN codes with per-(block,
+    kv head) scales)."""
+    if kv_dtype is not None:
+        code = KV_DTYPES.get(kv_dtype, kv_dtype)
+        one_byte = cache.dtype in _FP8_CODES or cache.dtype == torch.int8
+        if (code == PKV_BF16) == one_byte or code not in KV_DTYPES.values():
+            raise TypeError(f"cache dtype {cache.dtype} does not hold kv_dtype {kv_dtype!r}")
+        return code
     if cache.dtype in _BF16_BITS:
         return PKV_BF16
     if cache.dtype in _FP8_CODES:
@@ -129,7 +140,7 @@ def _stream(stream):
 
 
 def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
-                    k_scale=None, v_scale=None, stream=None) -> None:
+                    k_scale=None, v_scale=None, kv_dtype=None, stream=None) -> None:
     """k_new/v_new [B, Hkv, D] bf16; caches [num_blocks, block_size, Hkv, D]
     (bf16 bits or E4M3FN codes); block_tables [B, max_blocks] int32;
     context_lens [B] int32 (including the new token)."""
@@ -142,13 +153,14 @@ def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, 
     st = _lib.paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                               _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                               block_tables.shape[1], _ptr(context_lens), B, Hkv, D, bs, nb,
-                              _kv_dtype(k_cache), _stream(stream))
+                              _kv_dtype(k_cache, kv_dtype), _stream(stream))
     _check("paged_kv_append", st)
 
 
 def paged_decode_attention(query, k_cache, v_cache, block_tables, context_lens, scale, *,
                            out=None, lse_out=None, split_tokens=0, partial_out=None,
-                           partial_lse=None, k_scale=None, v_scale=None, stream=None):
+                           partial_lse=None, k_scale=None, v_scale=None, kv_dtype=None,
+                           stream=None):
     """query [B, Hq, D] bf16.  split_tokens == 0: writes out [B, Hq, D] float32
     (and lse_out [B, Hq]) and returns out.  split_tokens > 0: writes
     partial_out [B, Hq, max_splits, D] / partial_lse [B, Hq, max_splits] and
@@ -172,7 +184,7 @@ def paged_decode_attention(query, k_cache, v_cache, block_tables, context_lens, 
     st = _lib.paged_decode_attention(
         _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, nb,
-        _kv_dtype(k_cache), float(scale), int(split_tokens), _ptr(out), _ptr(partial_out),
+        _kv_dtype(k_cache, kv_dtype), float(scale), int(split_tokens), _ptr(out), _ptr(partial_out),
         _ptr(partial_lse), max_splits, _ptr(lse_out), _stream(stream))
     _check("paged_decode_attention", st)
     return out if split_tokens == 0 else (partial_out, partial_lse)
@@ -187,17 +199,17 @@ def paged_decode_workspace_size(Hq, Hkv, D, block_size, kv_dtype=PKV_BF16) -> in
     return n
 
 
-def make_workspace(query, k_cache) -> torch.Tensor:
+def make_workspace(query, k_cache, kv_dtype=None) -> torch.Tensor:
     """A device buffer large enough for paged_decode_attention_balanced."""
     B, Hq, D = query.shape
     n = paged_decode_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
-                                    _kv_dtype(k_cache))
+                                    _kv_dtype(k_cache, kv_dtype))
     return torch.empty(n, dtype=torch.uint8, device=query.device)
 
 
 def paged_decode_attention_balanced(query, k_cache, v_cache, block_tables, context_lens, scale,
                                     *, workspace, out=None, lse_out=None, k_scale=None,
-                                    v_scale=None, stream=None):
+                                    v_scale=None, kv_dtype=None, stream=None):
     """Single-pass paged decode attention with the work of all (sequence,
     kv head) pairs cut into equal ranges (for ragged batches).  workspace:
     a device buffer of paged_decode_workspace_size(...) bytes."""
@@ -213,7 +225,7 @@ def paged_decode_attention_balanced(query, k_cache, v_cache, block_tables, conte
     st = _lib.paged_decode_attention_balanced(
         _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, nb,
-        _kv_dtype(k_cache), float(scale), _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out),
+        _kv_dtype(k_cache, kv_dtype), float(scale), _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out),
         _stream(stream))
     _check("paged_decode_attention_balanced", st)
     return out
@@ -235,7 +247,8 @@ def split_context_reduce(partial_out, partial_lse, context_lens, split_tokens, *
 
 
 def paged_kv_write(k_rows, v_rows, query_start, k_cache, v_cache, block_tables, context_lens,
-                   max_query_len, *, k_scale=None, v_scale=None, stream=None) -> None:
+                   max_query_len, *, k_scale=None, v_scale=None, kv_dtype=None,
+                   stream=None) -> None:
     """k_rows/v_rows [rows, Hkv, D] bf16: rows query_start[b] + i go to
     positions context_lens[b] - q_b + i (q_b = query_start[b+1] -
     query_start[b] <= max_query_len)."""
@@ -252,7 +265,7 @@ def paged_kv_write(k_rows, v_rows, query_start, k_cache, v_cache, block_tables, 
     st = _lib.paged_kv_write(_ptr(k_rows), _ptr(v_rows), _ptr(query_start), _ptr(k_cache),
                              _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                              block_tables.shape[1], _ptr(context_lens), B, int(max_query_len),
-                             Hkv, D, bs, nb, _kv_dtype(k_cache), _stream(stream))
+                             Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), _stream(stream))
     _check("paged_kv_write", st)
 
 
@@ -267,17 +280,17 @@ def paged_multiquery_workspace_size(Hq, Hkv, D, block_size, max_query_len,
     return n
 
 
-def make_multiquery_workspace(query, k_cache, max_query_len) -> torch.Tensor:
+def make_multiquery_workspace(query, k_cache, max_query_len, kv_dtype=None) -> torch.Tensor:
     """A device buffer large enough for paged_multiquery_attention."""
     _, Hq, D = query.shape
     n = paged_multiquery_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
-                                        max_query_len, _kv_dtype(k_cache))
+                                        max_query_len, _kv_dtype(k_cache, kv_dtype))
     return torch.empty(n, dtype=torch.uint8, device=query.device)
 
 
 def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_tables, context_lens,
                                scale, max_query_len, *, workspace, out=None, lse_out=None,
-                               k_scale=None, v_scale=None, stream=None):
+                               k_scale=None, v_scale=None, kv_dtype=None, stream=None):
     """query [rows, Hq, D] bf16: row query_start[b] + i (position
     context_lens[b] - q_b + i) attends causally over its sequence's tokens
     up to its own position.  Writes out [rows, Hq, D] float32 (and lse_out
@@ -298,7 +311,7 @@ def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_table
     st = _lib.paged_multiquery_attention(
         _ptr(query), _ptr(query_start), rows, int(max_query_len), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), B, Hq, Hkv, D, bs, nb, _kv_dtype(k_cache), float(scale),
+        _ptr(context_lens), B, Hq, Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), float(scale),
         _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out), _stream(stream))
     _check("paged_multiquery_attention", st)
     return out
@@ -318,17 +331,18 @@ def _any_ptr(t):
     return t.data_ptr()
 
 
-def _move_shape(k_cache):
+def _move_shape(k_cache, kv_dtype=None):
     nb, bs, Hkv, D = k_cache.shape
-    return nb, bs, Hkv, D, _kv_dtype(k_cache)
+    return nb, bs, Hkv, D, _kv_dtype(k_cache, kv_dtype)
 
 
 def paged_kv_gather_blocks(k_cache, v_cache, block_ids, k_out, v_out, *, k_scale=None,
-                           v_scale=None, k_scale_out=None, v_scale_out=None, stream=None):
+                           v_scale=None, k_scale_out=None, v_scale_out=None, kv_dtype=None,
+                           stream=None):
     """k_out[i] = k_cache[block_ids[i]] (and V, and fp8 scales).  Outputs may
     be pinned host tensors (swap out / offload)."""
     _need(block_ids, (torch.int32,), "block_ids")
-    nb, bs, Hkv, D, dt = _move_shape(k_cache)
+    nb, bs, Hkv, D, dt = _move_shape(k_cache, kv_dtype)
     st = _lib.paged_kv_gather_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _any_ptr(block_ids),
         block_ids.numel(), bs, Hkv, D, nb, dt, _any_ptr(k_out), _any_ptr(v_out),
@@ -337,11 +351,12 @@ def paged_kv_gather_blocks(k_cache, v_cache, block_ids, k_out, v_out, *, k_scale
 
 
 def paged_kv_scatter_blocks(k_in, v_in, block_ids, k_cache, v_cache, *, k_scale_in=None,
-                            v_scale_in=None, k_scale=None, v_scale=None, stream=None):
+                            v_scale_in=None, k_scale=None, v_scale=None, kv_dtype=None,
+                            stream=None):
     """k_cache[block_ids[i]] = k_in[i] (and V, and fp8 scales).  Inputs may be
     pinned host tensors (swap in)."""
     _need(block_ids, (torch.int32,), "block_ids")
-    nb, bs, Hkv, D, dt = _move_shape(k_cache)
+    nb, bs, Hkv, D, dt = _move_shape(k_cache, kv_dtype)
     st = _lib.paged_kv_scatter_blocks(
         _any_ptr(k_in), _any_ptr(v_in), _any_ptr(k_scale_in), _any_ptr(v_scale_in),
         _any_ptr(block_ids), block_ids.numel(), bs, Hkv, D, nb, dt, _ptr(k_cache), _ptr(v_cache),
@@ -350,13 +365,13 @@ def paged_kv_scatter_blocks(k_in, v_in, block_ids, k_cache, v_cache, *, k_scale_
 
 
 def paged_kv_copy_blocks(k_cache, v_cache, src_ids, dst_ids, *, k_scale=None, v_scale=None,
-                         stream=None):
+                         kv_dtype=None, stream=None):
     """k_cache[dst_ids[i]] = k_cache[src_ids[i]] (copy-on-write copies)."""
     _need(src_ids, (torch.int32,), "src_ids")
     _need(dst_ids, (torch.int32,), "dst_ids")
     if src_ids.numel() != dst_ids.numel():
         raise ValueError("src_ids and dst_ids differ in length")
-    nb, bs, Hkv, D, dt = _move_shape(k_cache)
+    nb, bs, Hkv, D, dt = _move_shape(k_cache, kv_dtype)
     st = _lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                    _any_ptr(src_ids), _any_ptr(dst_ids), src_ids.numel(), bs, Hkv,
                                    D, nb, dt, _stream(stream))

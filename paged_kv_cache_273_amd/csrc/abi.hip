@@ -29,6 +29,40 @@ int launched(hipError_t e)
     return e == hipSuccess ? PKV_OK : PKV_ELAUNCH;
 }
 
+bool valid_dtype(int32_t kv_dtype)
+{
+    return kv_dtype >= PKV_BF16 && kv_dtype <= PKV_INT8;
+}
+
+bool one_byte(int32_t kv_dtype)
+{
+    return kv_dtype != PKV_BF16;
+}
+
+// Kernel format (0 bf16, 1 E4M3FN, 2 uint8 + zero point) and where the
+// scale of (block p, kv head h) lives: k_scale[p * sc_blk + h * sc_head].
+struct Fmt {
+    int kvf, sc_blk, sc_head;
+};
+
+Fmt format_of(int32_t kv_dtype, int32_t Hkv)
+{
+    switch (kv_dtype) {
+    case PKV_FP8_E4M3: return {1, Hkv, 1};
+    case PKV_FP8_E4M3_PER_HEAD: return {1, 0, 1};
+    case PKV_FP8_E4M3_PER_TENSOR: return {1, 0, 0};
+    case PKV_INT8: return {2, 2 * Hkv, 2};
+    default: return {0, 0, 0};
+    }
+}
+
+// floats of one block's scale record that move with the block
+int32_t scales_per_block(int32_t kv_dtype, int32_t Hkv)
+{
+    return kv_dtype == PKV_FP8_E4M3 ? Hkv : kv_dtype == PKV_INT8 ? 2 * Hkv : 0;
+}
+
+
 constexpr int32_t kMaxGroup = 16;     // query heads per kv head (one MFMA column tile)
 // MI355X last-level (Infinity Cache / MALL) capacity.  A K+V pool that fits
 // may be re-read from it by the next call; larger pools are streamed.
@@ -46,7 +80,7 @@ bool stream_kv_loads(int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_
 #ifdef PKV_FORCE_LOAD_POLICY
     return PKV_FORCE_LOAD_POLICY != 0;
 #else
-    const int64_t esize = kv_dtype == PKV_FP8_E4M3 ? 1 : 2;
+    const int64_t esize = one_byte(kv_dtype) ? 1 : 2;
     const int64_t pool = 2 * (int64_t)num_blocks * block_size * Hkv * D * esize;
     return pool > kMallBytes;
 #endif
@@ -77,7 +111,7 @@ int paged_kv_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache,
 {
     if (B < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks <= 0)
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size))
         return PKV_EUNSUPPORTED;
@@ -85,11 +119,11 @@ int paged_kv_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache,
         return PKV_OK;
     if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !context_lens)
         return PKV_EINVAL;
-    const uintptr_t cache_align = kv_dtype == PKV_FP8_E4M3 ? 8 : 16;
+    const uintptr_t cache_align = one_byte(kv_dtype) ? 8 : 16;
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, cache_align)
         || !aligned(v_cache, cache_align))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    if (one_byte(kv_dtype) && (!k_scale || !v_scale))
         return PKV_EINVAL;
     pkv::AppendArgs a;
     a.k_new = k_new;
@@ -105,7 +139,10 @@ int paged_kv_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache,
     a.Hkv = Hkv;
     a.D = D;
     a.block_size = block_size;
-    a.kv_dtype = kv_dtype;
+    const Fmt f = format_of(kv_dtype, Hkv);
+    a.kv_dtype = f.kvf;
+    a.sc_blk = f.sc_blk;
+    a.sc_head = f.sc_head;
     return launched(pkv::launch_append(a, (hipStream_t)stream));
 }
 
@@ -122,7 +159,7 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
         return PKV_EINVAL;
     if (Hq % Hkv != 0 || !isfinite(scale))
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
         return PKV_EUNSUPPORTED;
@@ -134,7 +171,7 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
         return PKV_EINVAL;
     if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    if (one_byte(kv_dtype) && (!k_scale || !v_scale))
         return PKV_EINVAL;
     if (split_tokens == 0) {
         if (!out || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
@@ -165,8 +202,11 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     a.split_tokens = split_tokens;
     a.max_splits = split_tokens > 0 ? max_splits : 1;
     a.scale_log2 = scale * 1.4426950408889634f;
+    const Fmt fmt = format_of(kv_dtype, Hkv);
+    a.sc_blk = fmt.sc_blk;
+    a.sc_head = fmt.sc_head;
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
-    return launched(pkv::launch_decode(a, D, block_size, kv_dtype, nt, (hipStream_t)stream));
+    return launched(pkv::launch_decode(a, D, block_size, fmt.kvf, nt, (hipStream_t)stream));
 }
 
 // Work-groups of the balanced decode on the current device: exactly the
@@ -179,7 +219,7 @@ static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t k
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     const int hg = pkv::balanced_head_group(Hkv);
-    return cus * pkv::balanced_groups_per_cu(D, block_size, kv_dtype, hg);
+    return cus * pkv::balanced_groups_per_cu(D, block_size, format_of(kv_dtype, Hkv).kvf, hg);
 }
 
 // Partial slots (2 per work-group) of rows_per_group rows, then the cut
@@ -211,7 +251,7 @@ int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t 
 {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
         return PKV_EUNSUPPORTED;
@@ -235,7 +275,7 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
         return PKV_EINVAL;
     if (Hq % Hkv != 0 || !isfinite(scale))
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
         return PKV_EUNSUPPORTED;
@@ -248,7 +288,7 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)
         || !aligned(out, 16) || !aligned(workspace, 16))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    if (one_byte(kv_dtype) && (!k_scale || !v_scale))
         return PKV_EINVAL;
     const int n = balanced_groups(Hkv, D, block_size, kv_dtype);
     if (n <= 0)
@@ -278,6 +318,9 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     a.split_tokens = 0;
     a.max_splits = 1;
     a.scale_log2 = scale * 1.4426950408889634f;
+    const Fmt fmt = format_of(kv_dtype, Hkv);
+    a.sc_blk = fmt.sc_blk;
+    a.sc_head = fmt.sc_head;
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv);
     ws.ngroups_launched = n;
@@ -289,7 +332,7 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     if (max_tiles * ((int64_t)n + 1) >= ((int64_t)1 << 52))
         return PKV_EUNSUPPORTED;
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
-    return launched(pkv::launch_decode_balanced(a, ws, D, block_size, kv_dtype, nt,
+    return launched(pkv::launch_decode_balanced(a, ws, D, block_size, fmt.kvf, nt,
                                                 (hipStream_t)stream));
 }
 
@@ -302,7 +345,7 @@ int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows, const int32_t
     if (B < 0 || max_query_len < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0
         || max_blocks <= 0)
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size))
         return PKV_EUNSUPPORTED;
@@ -313,11 +356,11 @@ int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows, const int32_t
     if (!k_rows || !v_rows || !query_start || !k_cache || !v_cache || !block_tables
         || !context_lens)
         return PKV_EINVAL;
-    const uintptr_t cache_align = kv_dtype == PKV_FP8_E4M3 ? 8 : 16;
+    const uintptr_t cache_align = one_byte(kv_dtype) ? 8 : 16;
     if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(k_cache, cache_align)
         || !aligned(v_cache, cache_align))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    if (one_byte(kv_dtype) && (!k_scale || !v_scale))
         return PKV_EINVAL;
     pkv::WriteArgs a;
     a.k_rows = k_rows;
@@ -335,7 +378,10 @@ int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows, const int32_t
     a.Hkv = Hkv;
     a.D = D;
     a.block_size = block_size;
-    a.kv_dtype = kv_dtype;
+    const Fmt f = format_of(kv_dtype, Hkv);
+    a.kv_dtype = f.kvf;
+    a.sc_blk = f.sc_blk;
+    a.sc_head = f.sc_head;
     return launched(pkv::launch_write(a, (hipStream_t)stream));
 }
 
@@ -354,7 +400,8 @@ static int mq_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtyp
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     const int hg = pkv::balanced_head_group(Hkv);
-    return cus * pkv::multiquery_groups_per_cu(D, block_size, kv_dtype, hg, nct);
+    return cus * pkv::multiquery_groups_per_cu(D, block_size, format_of(kv_dtype, Hkv).kvf, hg,
+                                                nct);
 }
 
 static int64_t mq_bytes(int ngroups, int32_t Hkv, int nct, int32_t D)
@@ -367,7 +414,7 @@ int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int3
 {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_query_len < 0)
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup
         || (int64_t)max_query_len > kMaxTokens)
@@ -394,7 +441,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
         return PKV_EINVAL;
     if (Hq % Hkv != 0 || !isfinite(scale))
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
     if (!supported_d(D) || !supported_bs(block_size) || Hq / Hkv > kMaxGroup)
         return PKV_EUNSUPPORTED;
@@ -410,7 +457,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)
         || !aligned(out, 16) || !aligned(workspace, 16) || (lse_out && !aligned(lse_out, 4)))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    if (one_byte(kv_dtype) && (!k_scale || !v_scale))
         return PKV_EINVAL;
     const int32_t G = Hq / Hkv;
     const int nct = mq_tiles_per_wave(max_query_len, G);
@@ -441,6 +488,9 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     a.split_tokens = 0;
     a.max_splits = 1;
     a.scale_log2 = scale * 1.4426950408889634f;
+    const Fmt fmt = format_of(kv_dtype, Hkv);
+    a.sc_blk = fmt.sc_blk;
+    a.sc_head = fmt.sc_head;
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv);
     ws.ngroups_launched = n;
@@ -454,7 +504,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     if (max_tiles * ((int64_t)n + 1) >= ((int64_t)1 << 52))
         return PKV_EUNSUPPORTED;
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
-    return launched(pkv::launch_multiquery(a, ws, D, block_size, kv_dtype, nct, nt,
+    return launched(pkv::launch_multiquery(a, ws, D, block_size, fmt.kvf, nct, nt,
                                            (hipStream_t)stream));
 }
 
@@ -464,14 +514,14 @@ static int move_checks(int32_t n, int32_t block_size, int32_t Hkv, int32_t D, in
 {
     if (n < 0 || block_size <= 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0)
         return PKV_EINVAL;
-    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    if (!valid_dtype(kv_dtype))
         return PKV_EINVAL;
-    const int64_t esize = kv_dtype == PKV_FP8_E4M3 ? 1 : 2;
+    const int64_t esize = one_byte(kv_dtype) ? 1 : 2;
     a.block_bytes = (int64_t)block_size * Hkv * D * esize;
     if (a.block_bytes % 16 != 0)
         return PKV_EUNSUPPORTED;
     a.n = n;
-    a.scale_count = kv_dtype == PKV_FP8_E4M3 ? Hkv : 0;
+    a.scale_count = scales_per_block(kv_dtype, Hkv);
     return PKV_OK;
 }
 
@@ -494,7 +544,7 @@ int paged_kv_gather_blocks(const void* k_cache, const void* v_cache, const float
         return PKV_EINVAL;
     if (!moves_aligned(k_cache, v_cache, k_out, v_out))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale || !k_scale_out || !v_scale_out))
+    if (a.scale_count > 0 && (!k_scale || !v_scale || !k_scale_out || !v_scale_out))
         return PKV_EINVAL;
     a.src_k = (const unsigned char*)k_cache;
     a.src_v = (const unsigned char*)v_cache;
@@ -523,7 +573,7 @@ int paged_kv_scatter_blocks(const void* k_in, const void* v_in, const float* k_s
         return PKV_EINVAL;
     if (!moves_aligned(k_in, v_in, k_cache, v_cache))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale || !k_scale_in || !v_scale_in))
+    if (a.scale_count > 0 && (!k_scale || !v_scale || !k_scale_in || !v_scale_in))
         return PKV_EINVAL;
     a.src_k = (const unsigned char*)k_in;
     a.src_v = (const unsigned char*)v_in;
@@ -551,7 +601,7 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_
         return PKV_EINVAL;
     if (!moves_aligned(k_cache, v_cache, k_cache, v_cache))
         return PKV_EINVAL;
-    if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    if (a.scale_count > 0 && (!k_scale || !v_scale))
         return PKV_EINVAL;
     a.src_k = (const unsigned char*)k_cache;
     a.src_v = (const unsigned char*)v_cache;

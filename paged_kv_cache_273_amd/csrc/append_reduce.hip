@@ -18,18 +18,51 @@ namespace {
 // sequence, i.e. slot (T-1) % bs of the physical block the table names for
 // logical block (T-1) / bs ([B] "PagedAttention").
 // One thread moves 8 elements (16 bytes of bf16 input) of one (b, h) row.
-// fp8 ([B] "FP8 KV cache"): code = E4M3FN(float(x) / scale[p, h]) with a
-// correctly rounded binary32 division.
+// fp8 ([B] "FP8 KV cache"): code = E4M3FN(float(x) / scale) with a
+// correctly rounded binary32 division; int8: see f32_to_u8_zp.
+// INT8 ([B] "INT8 KV cache"): code = clamp(rint(x / scale) + zero point,
+// 0, 255) with a correctly rounded binary32 division and round-half-even;
+// NaN gives 0.
+__device__ __forceinline__ uint32_t f32_to_u8_zp(float x, float scale, float zp)
+{
+    const float y = x / scale;
+    if (y != y)
+        return 0u;
+    const float v = __builtin_rintf(y) + zp;
+    return (uint32_t)fminf(fmaxf(v, 0.f), 255.f);
+}
+
+// Scales (and int8 zero points) of one (block, kv head).
+struct Quant {
+    float ks, vs, kz, vz;
+};
+
+template <int KVF>
+__device__ __forceinline__ Quant quant_of(const float* k_scale, const float* v_scale, int p,
+                                          int h, int sc_blk, int sc_head)
+{
+    Quant q = {1.f, 1.f, 0.f, 0.f};
+    if (KVF) {
+        const size_t i = (size_t)p * sc_blk + (size_t)h * sc_head;
+        q.ks = k_scale[i];
+        q.vs = v_scale[i];
+        if (KVF == 2) {
+            q.kz = k_scale[i + 1];
+            q.vz = v_scale[i + 1];
+        }
+    }
+    return q;
+}
+
 // Moves 8 elements (16 bytes of bf16 input) of one K row and one V row
-// into the cache at element offset dst (block scales ks / vs for fp8).
-template <int FP8>
+// into the cache at element offset dst, encoding for 1-byte formats.
+template <int KVF>
 __device__ __forceinline__ void store8(const uint16_t* k_src, const uint16_t* v_src,
-                                       void* k_cache, void* v_cache, size_t dst, float ks,
-                                       float vs)
+                                       void* k_cache, void* v_cache, size_t dst, Quant q)
 {
     const u32x4 kx = *(const u32x4*)k_src;
     const u32x4 vx = *(const u32x4*)v_src;
-    if (!FP8) {
+    if (!KVF) {
         *(u32x4*)((uint16_t*)k_cache + dst) = kx;
         *(u32x4*)((uint16_t*)v_cache + dst) = vx;
         return;
@@ -37,10 +70,16 @@ __device__ __forceinline__ void store8(const uint16_t* k_src, const uint16_t* v_
     u32x2 kq = {0u, 0u}, vq = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t kb = (kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t vb = (vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t kc = f32_to_e4m3_sat(bf16_bits_to_f32(kb) / ks);
-        const uint32_t vc = f32_to_e4m3_sat(bf16_bits_to_f32(vb) / vs);
+        const float kf = bf16_bits_to_f32((kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        const float vf = bf16_bits_to_f32((vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        uint32_t kc, vc;
+        if (KVF == 1) {
+            kc = f32_to_e4m3_sat(kf / q.ks);
+            vc = f32_to_e4m3_sat(vf / q.vs);
+        } else {
+            kc = f32_to_u8_zp(kf, q.ks, q.kz);
+            vc = f32_to_u8_zp(vf, q.vs, q.vz);
+        }
         kq[i / 4] |= kc << (8 * (i & 3));
         vq[i / 4] |= vc << (8 * (i & 3));
     }
@@ -48,7 +87,7 @@ __device__ __forceinline__ void store8(const uint16_t* k_src, const uint16_t* v_
     *(u32x2*)((uint8_t*)v_cache + dst) = vq;
 }
 
-template <int FP8>
+template <int KVF>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 {
     const int per_row = a.D / 8;
@@ -67,12 +106,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     const int slot = t % a.block_size;
     const size_t src = ((size_t)b * a.Hkv + h) * a.D + 8 * c;
     const size_t dst = (((size_t)p * a.block_size + slot) * a.Hkv + h) * a.D + 8 * c;
-    float ks = 1.f, vs = 1.f;
-    if (FP8) {
-        ks = a.k_scale[(size_t)p * a.Hkv + h];
-        vs = a.v_scale[(size_t)p * a.Hkv + h];
-    }
-    store8<FP8>(a.k_new + src, a.v_new + src, a.k_cache, a.v_cache, dst, ks, vs);
+    store8<KVF>(a.k_new + src, a.v_new + src, a.k_cache, a.v_cache, dst,
+                quant_of<KVF>(a.k_scale, a.v_scale, p, h, a.sc_blk, a.sc_head));
 }
 
 // ---------------------------------------------------------------- write
@@ -80,7 +115,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 // Batching"; draft tokens under verification): row query_start[b] + i goes
 // to position T_b - q_b + i.  Grid (x: rows i x heads x 8-element chunks
 // up to max_query_len rows, y: sequence b); threads past q_b exit.
-template <int FP8>
+template <int KVF>
 __global__ __launch_bounds__(256) void write_kernel(WriteArgs a)
 {
     const int per_row = a.D / 8;
@@ -100,12 +135,8 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a)
     const int slot = t % a.block_size;
     const size_t src = ((size_t)(row0 + i) * a.Hkv + h) * a.D + 8 * c;
     const size_t dst = (((size_t)p * a.block_size + slot) * a.Hkv + h) * a.D + 8 * c;
-    float ks = 1.f, vs = 1.f;
-    if (FP8) {
-        ks = a.k_scale[(size_t)p * a.Hkv + h];
-        vs = a.v_scale[(size_t)p * a.Hkv + h];
-    }
-    store8<FP8>(a.k_rows + src, a.v_rows + src, a.k_cache, a.v_cache, dst, ks, vs);
+    store8<KVF>(a.k_rows + src, a.v_rows + src, a.k_cache, a.v_cache, dst,
+                quant_of<KVF>(a.k_scale, a.v_scale, p, h, a.sc_blk, a.sc_head));
 }
 
 // ---------------------------------------------------------------- reduce
@@ -211,7 +242,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream)
     const long long blocks = (total + 255) / 256;
     if (blocks > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
-    if (a.kv_dtype == 1)
+    if (a.kv_dtype == 2)
+        hipLaunchKernelGGL(append_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (a.kv_dtype == 1)
         hipLaunchKernelGGL(append_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(append_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
@@ -227,7 +260,9 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t stream)
     if (blocks > 0x7FFFFFFFLL || a.B > 65535)
         return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks, (unsigned)a.B);
-    if (a.kv_dtype == 1)
+    if (a.kv_dtype == 2)
+        hipLaunchKernelGGL(write_kernel<2>, grid, dim3(256), 0, stream, a);
+    else if (a.kv_dtype == 1)
         hipLaunchKernelGGL(write_kernel<1>, grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(write_kernel<0>, grid, dim3(256), 0, stream, a);

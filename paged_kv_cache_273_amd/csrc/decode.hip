@@ -42,9 +42,14 @@
 // multiplication, keeps it out).  Block-table entries past the last live
 // block are never dereferenced.
 //
-// FP8 ([B] "FP8 KV cache"): E4M3FN codes convert exactly to bf16; the
-// per-(block, kv head) scale multiplies the block's scores (K) and the
-// block's probabilities before the PV product (V).
+// 1-byte caches (template KVF: 0 bf16, 1 E4M3FN, 2 uint8 with a zero
+// point).  FP8 ([B] "FP8 KV cache"): E4M3FN codes convert exactly to bf16;
+// the scale (per block and kv head, per kv head or per tensor: the index
+// strides sc_blk / sc_head select it) multiplies the block's scores (K) and
+// the block's probabilities before the PV product (V).  INT8 ([B] "INT8 KV
+// cache"): code u stands for scale * (u - zero point); u - zp is an
+// integer of magnitude <= 255, exact in bf16, and the scale enters as for
+// fp8.
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
 
@@ -76,12 +81,12 @@ __device__ __forceinline__ u32x4 load_kv(const unsigned char* p)
     return *(const u32x4*)p;
 }
 
-template <int D, int FP8>
+template <int D, int KVF>
 struct Cfg {
-    static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per cached element
+    static constexpr int ESZ = KVF ? 1 : 2;            // bytes per cached element
     static constexpr int ROW_BYTES = D * ESZ;           // one token of one kv head
     static constexpr int KSTEPS = D / 32;               // MFMA k-steps of q . k
-    static constexpr int K_LOADS = FP8 ? D / 64 : D / 32;  // 16-B loads per lane per 16 tokens
+    static constexpr int K_LOADS = KVF ? D / 64 : D / 32;  // 16-B loads per lane per 16 tokens
     static constexpr int V_LPR = ROW_BYTES / 16;        // lanes per V row
     static constexpr int V_RPI = kWave / V_LPR;         // V rows per load instruction
     static constexpr int V_LOADS = kTile / V_RPI;       // V loads per tile
@@ -96,20 +101,20 @@ struct Cfg {
 // wave has several column tiles (their registers would not fit beside the
 // accumulators and the tile in flight; each lane reads back only what it
 // wrote, so the slice needs no barrier).
-template <int D, int FP8, int NCT>
+template <int D, int KVF, int NCT>
 constexpr int wave_lds_bytes()
 {
-    return Cfg<D, FP8>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, FP8>::Q_BYTES : 0);
+    return Cfg<D, KVF>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, KVF>::Q_BYTES : 0);
 }
 
 // First of the 8 consecutive head-dim elements that lane group q feeds to
 // MFMA k-step j.  bf16: one 16-byte load per k-step (chunk q + 4j of
 // 8 elements).  fp8: one 16-byte load holds two k-steps (chunk q + 4c of
 // 16 codes, c = j / 2, low or high half).
-template <int FP8>
+template <int KVF>
 __device__ __forceinline__ int kdim_base(int j, int q)
 {
-    return FP8 ? 16 * (q + 4 * (j >> 1)) + 8 * (j & 1) : 8 * (q + 4 * j);
+    return KVF ? 16 * (q + 4 * (j >> 1)) + 8 * (j & 1) : 8 * (q + 4 * j);
 }
 
 // Token (within the 32-token tile) held in contraction slot (q, i) of the
@@ -120,16 +125,27 @@ __device__ __forceinline__ int pv_token(int q, int i)
     return i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4);
 }
 
-template <int D, int FP8>
+template <int D, int KVF>
 struct Tile {
-    u32x4 k[2][Cfg<D, FP8>::K_LOADS];
-    u32x4 v[Cfg<D, FP8>::V_LOADS];
+    u32x4 k[2][Cfg<D, KVF>::K_LOADS];
+    u32x4 v[Cfg<D, KVF>::V_LOADS];
 };
 
 struct TileAddr {
     int pA, pB;            // physical blocks of tokens 0..15 / 16..31
     float ksA, ksB, vsA, vsB;
+    float kzA, kzB, vzA, vzB;   // int8 zero points
 };
+
+// 16 cached bytes -> 16 bf16 MFMA operand elements (two 8-element halves).
+template <int KVF>
+__device__ __forceinline__ void codes_to_bf16(u32x4 raw, float zp, u32x4& lo, u32x4& hi)
+{
+    if (KVF == 1)
+        fp8x16_to_bf16x16(raw, lo, hi);
+    else
+        u8x16_to_bf16x16(raw, zp, lo, hi);
+}
 
 // Unnormalised result of attending one token range: fp32 accumulators in
 // the O^T layout (lane (q, r): O^T[16dt + 4q + i][r]), the running max in
@@ -169,12 +185,12 @@ __device__ __forceinline__ Cols<1> decode_cols(const DecodeArgs& a, int b, int h
 // tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.  With
 // CAUSAL, tokens at or past a column's limit are masked as well; a column
 // that sees no token of the range ends with l = 0.
-template <int D, int BS, int FP8, int NT, int NCT, bool CAUSAL>
+template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
                                              int h, int t_begin, int t_end,
                                              const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT])
 {
-    using C = Cfg<D, FP8>;
+    using C = Cfg<D, KVF>;
     const int lane = __lane_id();
     const int q4 = lane >> 4;
     const int r16 = lane & 15;
@@ -190,7 +206,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     for (int j = 0; j < NCT; ++j)
 #pragma unroll
         for (int k = 0; k < C::KSTEPS; ++k) {
-            u32x4 v = *(const u32x4*)(cs.qrow[j] + kdim_base<FP8>(k, q4));
+            u32x4 v = *(const u32x4*)(cs.qrow[j] + kdim_base<KVF>(k, q4));
             if (!cs.live[j])
                 v = u32x4{0u, 0u, 0u, 0u};
             if (QLDS)
@@ -253,15 +269,23 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             ta.pA = phys(t0 / 32);
             ta.pB = ta.pA;
         }
-        if (FP8) {
-            ta.ksA = a.k_scale[(size_t)ta.pA * Hkv + h];
-            ta.vsA = a.v_scale[(size_t)ta.pA * Hkv + h];
-            ta.ksB = a.k_scale[(size_t)ta.pB * Hkv + h];
-            ta.vsB = a.v_scale[(size_t)ta.pB * Hkv + h];
+        if (KVF) {
+            const size_t iA = (size_t)ta.pA * a.sc_blk + (size_t)h * a.sc_head;
+            const size_t iB = (size_t)ta.pB * a.sc_blk + (size_t)h * a.sc_head;
+            ta.ksA = a.k_scale[iA];
+            ta.vsA = a.v_scale[iA];
+            ta.ksB = a.k_scale[iB];
+            ta.vsB = a.v_scale[iB];
+            if (KVF == 2) {
+                ta.kzA = a.k_scale[iA + 1];
+                ta.vzA = a.v_scale[iA + 1];
+                ta.kzB = a.k_scale[iB + 1];
+                ta.vzB = a.v_scale[iB + 1];
+            }
         }
         return ta;
     };
-    auto load_k = [&](const TileAddr& ta, Tile<D, FP8>& tl) {
+    auto load_k = [&](const TileAddr& ta, Tile<D, KVF>& tl) {
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             const unsigned char* blk = kc + (size_t)(tau ? ta.pB : ta.pA) * blk_stride;
@@ -270,7 +294,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                 tl.k[tau][c] = load_kv<NT>(blk + k_off[tau] + 64 * c);
         }
     };
-    auto load_v = [&](const TileAddr& ta, Tile<D, FP8>& tl) {
+    auto load_v = [&](const TileAddr& ta, Tile<D, KVF>& tl) {
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
             const int p = (BS == 16 && k * C::V_RPI >= 16) ? ta.pB : ta.pA;
@@ -290,17 +314,25 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     const float sl2 = a.scale_log2;
 
     // V rows -> LDS as bf16 (zeroed past the range end).
-    auto stage_v = [&](int t0, const Tile<D, FP8>& tl, bool masked) {
+    auto stage_v = [&](int t0, const TileAddr& ta, const Tile<D, KVF>& tl, bool masked) {
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
             const int rr = k * C::V_RPI + lane / C::V_LPR;
             const int c = lane % C::V_LPR;
             u32x4 v = tl.v[k];
-            if (masked && t0 + rr >= t_end)
+            float zp = 0.f;
+            if (KVF == 2)
+                zp = (BS == 16 && k * C::V_RPI >= 16) ? ta.vzB : ta.vzA;
+            const bool dead = masked && t0 + rr >= t_end;
+            if (dead)
                 v = u32x4{0u, 0u, 0u, 0u};
-            if (FP8) {
+            if (KVF) {
                 u32x4 lo, hi;
-                fp8x16_to_bf16x16(v, lo, hi);
+                codes_to_bf16<KVF>(v, zp, lo, hi);
+                if (KVF == 2 && dead) {
+                    lo = u32x4{0u, 0u, 0u, 0u};
+                    hi = u32x4{0u, 0u, 0u, 0u};
+                }
                 u32x2* dst = (u32x2*)(lds + rr * C::PITCH + 32 * c);
                 dst[0] = u32x2{lo[0], lo[1]};
                 dst[1] = u32x2{lo[2], lo[3]};
@@ -316,7 +348,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
 
     // scores S^T[token][column] of the two 16-token halves, every column
     // tile sharing each K operand
-    auto qk = [&](const Tile<D, FP8>& tl, f32x4 (&sacc)[NCT][2]) {
+    auto qk = [&](const TileAddr& ta, const Tile<D, KVF>& tl, f32x4 (&sacc)[NCT][2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
@@ -324,9 +356,9 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                 sacc[j][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < C::K_LOADS; ++c) {
-                if (FP8) {
+                if (KVF) {
                     u32x4 lo, hi;
-                    fp8x16_to_bf16x16(tl.k[tau][c], lo, hi);
+                    codes_to_bf16<KVF>(tl.k[tau][c], tau ? ta.kzB : ta.kzA, lo, hi);
 #pragma unroll
                     for (int j = 0; j < NCT; ++j) {
                         sacc[j][tau] = mfma_16x16x32(as_bf16x8(lo), qop(j, 2 * c), sacc[j][tau]);
@@ -353,7 +385,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             float s[8];
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
-                const float f = FP8 ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
+                const float f = KVF ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = sacc[j][tau][i] * f;
@@ -385,7 +417,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
                 r[j].acc[dt] *= alpha;
-            if (FP8) {
+            if (KVF) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     p[i] *= ta.vsA;
@@ -432,17 +464,17 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     int n_plain = ntiles - 1;
     if (CAUSAL)
         n_plain = max(0, min(n_plain, (min(t_end, cs.mask_from) - t_begin) / kTile));
-    Tile<D, FP8> tl;
+    Tile<D, KVF> tl;
     TileAddr ta = tile_addr(t_begin);
     load_k(ta, tl);
     load_v(ta, tl);
     auto step = [&](int it, bool masked) {
         const int t0 = t_begin + kTile * it;
         const TileAddr tn = tile_addr(t0 + kTile);
-        stage_v(t0, tl, false);
+        stage_v(t0, ta, tl, false);
         load_v(tn, tl);
         f32x4 sacc[NCT][2];
-        qk(tl, sacc);
+        qk(ta, tl, sacc);
         load_k(tn, tl);
         softmax_pv(t0, ta, sacc, masked);
         ta = tn;
@@ -454,9 +486,9 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             step(it, true);
     {
         const int t0 = t_begin + kTile * (ntiles - 1);
-        stage_v(t0, tl, true);
+        stage_v(t0, ta, tl, true);
         f32x4 sacc[NCT][2];
-        qk(tl, sacc);
+        qk(ta, tl, sacc);
         softmax_pv(t0, ta, sacc, true);
     }
 }
@@ -494,11 +526,11 @@ __device__ __forceinline__ void store_empty_row(float* o)
 
 // Fixed partition: one wave per (b, h) over the whole context, or per
 // (b, h, split) over [s * split_tokens, min(T, (s + 1) * split_tokens)).
-template <int D, int BS, int FP8, int NT, bool SPLIT>
+template <int D, int BS, int KVF, int NT, bool SPLIT>
 __global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_kernel(DecodeArgs a)
 {
-    using C = Cfg<D, FP8>;
+    using C = Cfg<D, KVF>;
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
 
     const int q4 = __lane_id() >> 4;
@@ -534,7 +566,7 @@ void decode_kernel(DecodeArgs a)
         return;
     }
     RangeAcc<D> r[1];
-    attend_range<D, BS, FP8, NT, 1, false>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin,
+    attend_range<D, BS, KVF, NT, 1, false>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin,
                                            t_end, decode_cols(a, b, h, D), r);
     float inv, lse;
     finish_range<D>(r[0], inv, lse);
@@ -652,11 +684,11 @@ __device__ __forceinline__ long long range_start(long long r, long long total, l
     return (long long)__builtin_floor((double)(r * total) / (double)R);
 }
 
-template <int D, int BS, int FP8, int NT, int NCT, bool MQ>
+template <int D, int BS, int KVF, int NT, int NCT, bool MQ>
 __global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 {
-    using C = Cfg<D, FP8>;
+    using C = Cfg<D, KVF>;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_all[];  // HG slices
 
     const int q4 = __lane_id() >> 4;
@@ -685,7 +717,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     int n = tiles_of(T);
     int ncg = col_groups<MQ, NCT>(a, b);
     int u = (int)((r0 - before * ngroups) / n);      // unit of b: hg * ncg + cg
-    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, FP8, NCT>();
+    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, KVF, NCT>();
     const int rows_per_slot = HG * cpw;
     long long x = r0;
     int piece = 0;
@@ -702,7 +734,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         const size_t slot = 2 * (size_t)r + (piece == 0 ? 0 : 1);
         if (!MQ) {
             RangeAcc<D> acc[1];
-            attend_range<D, BS, FP8, NT, 1, false>(a, lds, b, h, t_begin, t_end,
+            attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
                                                    decode_cols(a, b, h, D), acc);
             float inv, lse;
             finish_range<D>(acc[0], inv, lse);
@@ -736,7 +768,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
             }
             cs.mask_from = T - q + (cg * kCols) / G + 1;
             RangeAcc<D> acc[NCT];
-            attend_range<D, BS, FP8, NT, NCT, true>(a, lds, b, h, t_begin, t_end, cs, acc);
+            attend_range<D, BS, KVF, NT, NCT, true>(a, lds, b, h, t_begin, t_end, cs, acc);
 #pragma unroll
             for (int j = 0; j < NCT; ++j) {
                 float inv, lse;
@@ -934,30 +966,30 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
         a.lse_out[orow] = m + __logf(wsum);
 }
 
-template <int D, int BS, int FP8, int NCT, bool MQ>
+template <int D, int BS, int KVF, int NCT, bool MQ>
 int balanced_occupancy(int head_group)
 {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks,
-            reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, FP8, 1, NCT, MQ>),
-            head_group * kWave, (size_t)head_group * wave_lds_bytes<D, FP8, NCT>())
+            reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>),
+            head_group * kWave, (size_t)head_group * wave_lds_bytes<D, KVF, NCT>())
         != hipSuccess)
         return 0;
     return blocks;
 }
 
-template <int D, int BS, int FP8, int NCT, bool MQ>
+template <int D, int BS, int KVF, int NCT, bool MQ>
 hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt,
                              hipStream_t stream)
 {
-    const size_t lds = (size_t)ws.head_group * wave_lds_bytes<D, FP8, NCT>();
+    const size_t lds = (size_t)ws.head_group * wave_lds_bytes<D, KVF, NCT>();
     const dim3 grid((unsigned)ws.ngroups_launched), block(ws.head_group * kWave);
     if (nt)
-        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 1, NCT, MQ>), grid, block, lds,
+        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>), grid, block, lds,
                            stream, a, ws);
     else
-        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, FP8, 0, NCT, MQ>), grid, block, lds,
+        hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 0, NCT, MQ>), grid, block, lds,
                            stream, a, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -970,7 +1002,7 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt
     return hipGetLastError();
 }
 
-template <int D, int BS, int FP8, int NT>
+template <int D, int BS, int KVF, int NT>
 hipError_t launch_fixed_t(const DecodeArgs& a, hipStream_t stream)
 {
     const bool split = a.split_tokens > 0;
@@ -982,16 +1014,16 @@ hipError_t launch_fixed_t(const DecodeArgs& a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)groups), block(kWavesPerGroup * kWave);
     if (split)
-        hipLaunchKernelGGL((decode_kernel<D, BS, FP8, NT, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, BS, FP8, NT, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, int BS, int FP8>
+template <int D, int BS, int KVF>
 hipError_t launch_fixed_d_bs_dt(const DecodeArgs& a, bool nt, hipStream_t stream)
 {
-    return nt ? launch_fixed_t<D, BS, FP8, 1>(a, stream) : launch_fixed_t<D, BS, FP8, 0>(a, stream);
+    return nt ? launch_fixed_t<D, BS, KVF, 1>(a, stream) : launch_fixed_t<D, BS, KVF, 0>(a, stream);
 }
 
 } // namespace
@@ -1008,8 +1040,9 @@ int balanced_groups_per_cu(int D, int block_size, int kv_dtype, int head_group)
 {
 #define PKV_OCC(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1, 1, false>(head_group)      \
-                             : balanced_occupancy<d, bs, 0, 1, false>(head_group);
+        return kv_dtype == 2   ? balanced_occupancy<d, bs, 2, 1, false>(head_group)    \
+               : kv_dtype == 1 ? balanced_occupancy<d, bs, 1, 1, false>(head_group)    \
+                               : balanced_occupancy<d, bs, 0, 1, false>(head_group);
     PKV_OCC(128, 16)
     PKV_OCC(128, 32)
     PKV_OCC(64, 16)
@@ -1023,8 +1056,9 @@ hipError_t launch_decode_balanced(const DecodeArgs& a, const BalanceArgs& ws, in
 {
 #define PKV_BAL(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1, 1, false>(a, ws, nt, stream) \
-                             : launch_balanced_t<d, bs, 0, 1, false>(a, ws, nt, stream);
+        return kv_dtype == 2   ? launch_balanced_t<d, bs, 2, 1, false>(a, ws, nt, stream) \
+               : kv_dtype == 1 ? launch_balanced_t<d, bs, 1, 1, false>(a, ws, nt, stream) \
+                               : launch_balanced_t<d, bs, 0, 1, false>(a, ws, nt, stream);
     PKV_BAL(128, 16)
     PKV_BAL(128, 32)
     PKV_BAL(64, 16)
@@ -1037,8 +1071,9 @@ int multiquery_groups_per_cu(int D, int block_size, int kv_dtype, int head_group
 {
 #define PKV_MQOCC(d, bs, n)                                                             \
     if (D == d && block_size == bs && nct == n)                                        \
-        return kv_dtype == 1 ? balanced_occupancy<d, bs, 1, n, true>(head_group)       \
-                             : balanced_occupancy<d, bs, 0, n, true>(head_group);
+        return kv_dtype == 2   ? balanced_occupancy<d, bs, 2, n, true>(head_group)     \
+               : kv_dtype == 1 ? balanced_occupancy<d, bs, 1, n, true>(head_group)     \
+                               : balanced_occupancy<d, bs, 0, n, true>(head_group);
     PKV_MQOCC(128, 16, 1)
     PKV_MQOCC(128, 32, 1)
     PKV_MQOCC(64, 16, 1)
@@ -1056,8 +1091,9 @@ hipError_t launch_multiquery(const DecodeArgs& a, const BalanceArgs& ws, int D, 
 {
 #define PKV_MQ(d, bs, n)                                                                \
     if (D == d && block_size == bs && nct == n)                                        \
-        return kv_dtype == 1 ? launch_balanced_t<d, bs, 1, n, true>(a, ws, nt, stream)  \
-                             : launch_balanced_t<d, bs, 0, n, true>(a, ws, nt, stream);
+        return kv_dtype == 2   ? launch_balanced_t<d, bs, 2, n, true>(a, ws, nt, stream) \
+               : kv_dtype == 1 ? launch_balanced_t<d, bs, 1, n, true>(a, ws, nt, stream) \
+                               : launch_balanced_t<d, bs, 0, n, true>(a, ws, nt, stream);
     PKV_MQ(128, 16, 1)
     PKV_MQ(128, 32, 1)
     PKV_MQ(64, 16, 1)
@@ -1075,8 +1111,9 @@ hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtyp
 {
 #define PKV_FIX(d, bs)                                                                  \
     if (D == d && block_size == bs)                                                    \
-        return kv_dtype == 1 ? launch_fixed_d_bs_dt<d, bs, 1>(a, nt, stream)           \
-                             : launch_fixed_d_bs_dt<d, bs, 0>(a, nt, stream);
+        return kv_dtype == 2   ? launch_fixed_d_bs_dt<d, bs, 2>(a, nt, stream)         \
+               : kv_dtype == 1 ? launch_fixed_d_bs_dt<d, bs, 1>(a, nt, stream)         \
+                               : launch_fixed_d_bs_dt<d, bs, 0>(a, nt, stream);
     PKV_FIX(128, 16)
     PKV_FIX(128, 32)
     PKV_FIX(64, 16)

@@ -66,6 +66,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// 16 unsigned byte codes u -> 16 bf16 values u - zp, in byte order (low
+// half bytes 0-7, high half bytes 8-15).  Exact: zp is integer-valued in
+// [0, 255], so u - zp is an integer of magnitude <= 255.
+__device__ __forceinline__ void u8x16_to_bf16x16(u32x4 codes, float zp, u32x4& lo, u32x4& hi)
+{
+    uint32_t o[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t x = codes[w];
+        o[2 * w] = pack_bf16x2((float)(x & 0xFFu) - zp, (float)((x >> 8) & 0xFFu) - zp);
+        o[2 * w + 1] = pack_bf16x2((float)((x >> 16) & 0xFFu) - zp, (float)(x >> 24) - zp);
+    }
+    lo = u32x4{o[0], o[1], o[2], o[3]};
+    hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
 {
     return __builtin_bit_cast(float, bits16 << 16);

@@ -16,7 +16,8 @@ struct AppendArgs {
     const float* v_scale;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int32_t max_blocks, B, Hkv, D, block_size, kv_dtype;
+    int32_t max_blocks, B, Hkv, D, block_size, kv_dtype;   // kv_dtype: kernel format 0/1/2
+    int32_t sc_blk, sc_head;
 };
 
 struct DecodeArgs {
@@ -33,6 +34,7 @@ struct DecodeArgs {
     float* partial_lse;   // split
     const int32_t* query_start;  // several new tokens: [B + 1] row offsets, else null
     int32_t max_blocks, B, Hq, Hkv, G, split_tokens, max_splits;
+    int32_t sc_blk, sc_head;     // scale of (block p, head h): k_scale[p * sc_blk + h * sc_head]
     int32_t total_rows;   // several new tokens: rows of query / out
     float scale_log2;     // softmax scale * log2(e)
 };
@@ -70,7 +72,8 @@ struct WriteArgs {
     const float* v_scale;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int32_t max_blocks, B, max_query_len, Hkv, D, block_size, kv_dtype;
+    int32_t max_blocks, B, max_query_len, Hkv, D, block_size, kv_dtype;   // format 0/1/2
+    int32_t sc_blk, sc_head;
 };
 
 // Whole-block moves: destination block dst_ids[i] (i if null) of the
@@ -100,6 +103,9 @@ struct ReduceArgs {
     int32_t B, Hq, D, split_tokens, max_splits;
 };
 
+// Kernel formats: the C ABI's kv_dtype codes map to 0 (bf16), 1 (E4M3FN,
+// any scale granularity) or 2 (uint8 with zero point); the scale of block p,
+// kv head h is at [p * sc_blk + h * sc_head] (its zero point at + 1).
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // nt: stream the K/V loads with the non-temporal hint
 hipError_t launch_decode(const DecodeArgs& a, int D, int block_size, int kv_dtype, bool nt,

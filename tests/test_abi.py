@@ -88,8 +88,10 @@ def _decode(pkv, **kw):
     ({"D": 96}, -2),                     # head_dim outside the kernel set
     ({"bs": 8}, -2),                     # block size outside the kernel set
     ({"Hq": 64, "Hkv": 2}, -2),          # group of 32 query heads
-    ({"dt": 3}, -1),                     # unknown cache dtype
+    ({"dt": 5}, -1),                     # unknown cache dtype
     ({"dt": 1}, -1),                     # fp8 without scales
+    ({"dt": 3}, -1),                     # per-tensor fp8 without scale
+    ({"dt": 4}, -1),                     # int8 without scales
     ({"split": 24}, -1),                 # split not a multiple of the block size
     ({"split": 32, "ms": 0}, -1),        # split without partial slots
     ({"split": 32, "ms": 4}, -1),        # split without partial buffers
@@ -132,8 +134,9 @@ def _balanced(pkv, **kw):
     ({"D": 96}, -2),
     ({"bs": 64}, -2),
     ({"Hq": 64, "Hkv": 2}, -2),
-    ({"dt": 2}, -1),
+    ({"dt": 5}, -1),
     ({"dt": 1}, -1),                     # fp8 without scales
+    ({"dt": 4}, -1),                     # int8 without scales
     ({"ws": None}, -1),                  # no workspace
     ({"ws": 0x1004}, -1),                # misaligned workspace
     ({"wsb": -5}, -1),
@@ -209,8 +212,9 @@ def _mq(pkv, **kw):
     ({"D": 96}, -2),
     ({"bs": 64}, -2),
     ({"Hq": 64, "Hkv": 2}, -2),
-    ({"dt": 2}, -1),
+    ({"dt": 5}, -1),
     ({"dt": 1}, -1),                     # fp8 without scales
+    ({"dt": 4}, -1),                     # int8 without scales
     ({"ws": None}, -1),
     ({"ws": 0x1004}, -1),
     ({"qs": None}, -1),
@@ -237,6 +241,7 @@ def test_multiquery_workspace_size_rejects(pkv):
     assert L.paged_multiquery_workspace_size(8, 2, 96, 16, 0, 4) == -2
     assert L.paged_multiquery_workspace_size(8, 2, 64, 8, 0, 4) == -2
     assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 7, 4) == -1
+    assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 4, 4) != -1   # int8 is a format
     assert L.paged_multiquery_workspace_size(8, 2, 64, 16, 0, -1) == -1
 
 
@@ -253,7 +258,8 @@ def test_block_moves_reject(pkv):
     assert g(f, f, None, None, f, 0, 16, 2, 64, 8, 0, f, f, None, None, None) == 0
     s = L.paged_kv_scatter_blocks
     assert s(f, f, None, None, f, 4, 16, 2, 64, 0, 0, f, f, None, None, None) == -1  # no blocks
-    assert s(f, f, None, None, f, 4, 16, 2, 64, 8, 3, f, f, None, None, None) == -1  # dtype
+    assert s(f, f, None, None, f, 4, 16, 2, 64, 8, 9, f, f, None, None, None) == -1  # dtype
+    assert s(f, f, None, None, f, 4, 16, 2, 64, 8, 4, f, f, None, None, None) == -1  # int8, no scales
     c = L.paged_kv_copy_blocks
     assert c(f, f, None, None, f, None, 2, 16, 2, 64, 8, 0, None) == -1
     assert c(f, f, None, None, f, f, 0, 16, 2, 64, 8, 0, None) == 0
