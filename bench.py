@@ -13,9 +13,10 @@ already resident in HBM.
 
 Prints ONE JSON line.  value = KV-read GB/s of the whole step (ideal KV
 bytes 2 * sum(ctx) * Hkv * D * bytes_per_elem per layer call, times the
-layers, / step time).  roofline = one attention call, timed with HIP events
-on the stream it is launched on.  cpu_baseline = the CPU oracle on a bounded
-sample of the same workload, on this machine's host cores.
+layers, / step time).  roofline = one attention call per step (layer
+i mod layers in step i), timed with HIP events on the stream it is
+launched on.  cpu_baseline = the CPU oracle on a bounded sample of the
+same workload, on this machine's host cores.
 """
 from __future__ import annotations
 
@@ -179,7 +180,10 @@ def main():
     if mode == "multiquery":
         ws = pkv.make_multiquery_workspace(qs[0], caches[0][0], max_q, kv_dtype=fmt)
 
-    ev = []  # (start, end) around each attention call in the timed region
+    # (start, end) HIP events around one attention call per timed step: layer
+    # i % layers in step i, so every layer's call is sampled without putting
+    # two event records around each of the step's calls
+    ev = []
 
     def step(record):
         for k, v, ks, vs, kn, vn in caches:
@@ -191,7 +195,8 @@ def main():
         for layer in range(wl.layers):
             k, v, ks, vs, _, _ = caches[layer // wl.layers_per_group]
             q = qs[layer]
-            if record:
+            timed = record is not None and layer == record % wl.layers
+            if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
@@ -210,7 +215,7 @@ def main():
             else:
                 pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks,
                                            v_scale=vs, kv_dtype=fmt)
-            if record:
+            if timed:
                 e1.record()
                 ev.append((e0, e1))
             if mode == "split":
@@ -224,11 +229,11 @@ def main():
         del src, dst
 
     for _ in range(a.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step(True)
+    for i in range(a.steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3 / len(ev)

@@ -47,9 +47,13 @@
 // the scale (per block and kv head, per kv head or per tensor: the index
 // strides sc_blk / sc_head select it) multiplies the block's scores (K) and
 // the block's probabilities before the PV product (V).  INT8 ([B] "INT8 KV
-// cache"): code u stands for scale * (u - zero point); u - zp is an
-// integer of magnitude <= 255, exact in bf16, and the scale enters as for
-// fp8.
+// cache"): code u stands for scale * (u - zp).  With one column tile per
+// wave the codes enter the MFMA as the exact bf16 integers u (one
+// byte-to-float conversion each) and the zero points are applied outside
+// it: a score is scale_k * (q . u - zp_k * sum(q)), and the output
+// subtracts sum_t p_t * scale_v * zp_v, accumulated per column beside the
+// MFMA sums.  With two column tiles (whose registers are full) the codes
+// enter as the exact bf16 integers u - zp instead.
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
 
@@ -137,14 +141,15 @@ struct TileAddr {
     float kzA, kzB, vzA, vzB;   // int8 zero points
 };
 
-// 16 cached bytes -> 16 bf16 MFMA operand elements (two 8-element halves).
-template <int KVF>
+// 16 cached bytes -> 16 bf16 MFMA operand elements (two 8-element halves):
+// fp8 values; int8 codes u (zero point folded out of the MFMA) or u - zp.
+template <int KVF, bool FOLD>
 __device__ __forceinline__ void codes_to_bf16(u32x4 raw, float zp, u32x4& lo, u32x4& hi)
 {
     if (KVF == 1)
         fp8x16_to_bf16x16(raw, lo, hi);
     else
-        u8x16_to_bf16x16(raw, zp, lo, hi);
+        u8x16_to_bf16x16(raw, FOLD ? 0.f : zp, lo, hi);
 }
 
 // Unnormalised result of attending one token range: fp32 accumulators in
@@ -155,6 +160,7 @@ struct RangeAcc {
     f32x4 acc[D / 16];
     float m;
     float l;
+    float corr;     // int8: this lane's share of sum_t p_t * scale_v * zp_v
 };
 
 // The MFMA columns of one wave: NCT tiles of 16 columns, each column one
@@ -191,6 +197,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                                              const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT])
 {
     using C = Cfg<D, KVF>;
+    constexpr bool FOLD = KVF == 2 && NCT == 1;   // int8 zero points outside the MFMA
     const int lane = __lane_id();
     const int q4 = lane >> 4;
     const int r16 = lane & 15;
@@ -214,6 +221,26 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             else
                 qf[QLDS ? 0 : j][k] = as_bf16x8(v);
         }
+    // int8: sum of each column's query elements (lane groups q4 hold
+    // disjoint quarters of the head dimension)
+    float qsum[NCT];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+        qsum[j] = 0.f;
+        if (FOLD) {
+#pragma unroll
+            for (int k = 0; k < C::KSTEPS; ++k) {
+                const u32x4 v = *(const u32x4*)(cs.qrow[j] + kdim_base<KVF>(k, q4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    qsum[j] += bf16_bits_to_f32(v[e] & 0xFFFFu) + bf16_bits_to_f32(v[e] >> 16);
+            }
+            if (!cs.live[j])
+                qsum[j] = 0.f;
+            qsum[j] += xor_shuffle(qsum[j], 16);
+            qsum[j] += xor_shuffle(qsum[j], 32);
+        }
+    }
     auto qop = [&](int j, int k) -> bf16x8 {
         if (QLDS) {
             const u32x4 v = qlds[(j * C::KSTEPS + k) * kWave + lane];
@@ -310,6 +337,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             r[j].acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         r[j].m = -__builtin_inff();
         r[j].l = 0.f;
+        r[j].corr = 0.f;
     }
     const float sl2 = a.scale_log2;
 
@@ -320,16 +348,16 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             const int rr = k * C::V_RPI + lane / C::V_LPR;
             const int c = lane % C::V_LPR;
             u32x4 v = tl.v[k];
-            float zp = 0.f;
-            if (KVF == 2)
-                zp = (BS == 16 && k * C::V_RPI >= 16) ? ta.vzB : ta.vzA;
             const bool dead = masked && t0 + rr >= t_end;
             if (dead)
                 v = u32x4{0u, 0u, 0u, 0u};
             if (KVF) {
                 u32x4 lo, hi;
-                codes_to_bf16<KVF>(v, zp, lo, hi);
-                if (KVF == 2 && dead) {
+                float zp = 0.f;
+                if (KVF == 2 && !FOLD)
+                    zp = (BS == 16 && k * C::V_RPI >= 16) ? ta.vzB : ta.vzA;
+                codes_to_bf16<KVF, FOLD>(v, zp, lo, hi);
+                if (KVF == 2 && !FOLD && dead) {
                     lo = u32x4{0u, 0u, 0u, 0u};
                     hi = u32x4{0u, 0u, 0u, 0u};
                 }
@@ -358,7 +386,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             for (int c = 0; c < C::K_LOADS; ++c) {
                 if (KVF) {
                     u32x4 lo, hi;
-                    codes_to_bf16<KVF>(tl.k[tau][c], tau ? ta.kzB : ta.kzA, lo, hi);
+                    codes_to_bf16<KVF, FOLD>(tl.k[tau][c], tau ? ta.kzB : ta.kzA, lo, hi);
 #pragma unroll
                     for (int j = 0; j < NCT; ++j) {
                         sacc[j][tau] = mfma_16x16x32(as_bf16x8(lo), qop(j, 2 * c), sacc[j][tau]);
@@ -386,9 +414,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
                 const float f = KVF ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
+                const float zq = FOLD ? (tau ? ta.kzB : ta.kzA) * qsum[j] : 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float x = sacc[j][tau][i] * f;
+                    float x = (FOLD ? sacc[j][tau][i] - zq : sacc[j][tau][i]) * f;
                     if (masked && t0 + 16 * tau + 4 * q4 + i >= lim)
                         x = -__builtin_inff();
                     s[4 * tau + i] = x;
@@ -424,6 +453,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                     p[4 + i] *= ta.vsB;
                 }
             }
+            if (FOLD)
+                r[j].corr = r[j].corr * alpha
+                            + ta.vzA * ((p[0] + p[1]) + (p[2] + p[3]))
+                            + ta.vzB * ((p[4] + p[5]) + (p[6] + p[7]));
             // P as a two-term bf16 split, p = hi + lo (about 16 significant
             // bits): one bf16 term alone loses too much when V terms cancel.
             u32x4 pw, pr;
@@ -490,6 +523,17 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         f32x4 sacc[NCT][2];
         qk(ta, tl, sacc);
         softmax_pv(t0, ta, sacc, true);
+    }
+    if (FOLD) {
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+            float c = r[j].corr;
+            c += xor_shuffle(c, 16);
+            c += xor_shuffle(c, 32);
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                r[j].acc[dt] -= c;
+        }
     }
 }
 
@@ -684,6 +728,17 @@ __device__ __forceinline__ long long range_start(long long r, long long total, l
     return (long long)__builtin_floor((double)(r * total) / (double)R);
 }
 
+// The work-group whose range holds linear tile x.
+__device__ __forceinline__ long long range_of(long long x, long long total, long long R)
+{
+    long long r = (long long)((double)x * (double)R / (double)total);
+    while (r + 1 < R && range_start(r + 1, total, R) <= x)
+        ++r;
+    while (r > 0 && range_start(r, total, R) > x)
+        --r;
+    return r;
+}
+
 template <int D, int BS, int KVF, int NT, int NCT, bool MQ>
 __global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
@@ -704,7 +759,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
-    CutRecord cut = {-1, 0, 0, total, 0};
+    CutRecord cut = {0, total, 0, -1, 0, 0, 0, 0, 0};
     if (r0 >= r1) {
         if (threadIdx.x == 0)
             ws.cuts[r] = cut;
@@ -795,6 +850,13 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
                 cut.b = b;
                 cut.u = u;
                 cut.ustart = ustart;
+                cut.n = n;
+                cut.ncg = ncg;
+                cut.rl = range_of(uend - 1, total, R);
+                if (MQ) {
+                    cut.qs = a.query_start[b];
+                    cut.q = a.query_start[b + 1] - cut.qs;
+                }
             }
             break;
         }
@@ -852,17 +914,16 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
         }
         return;
     }
-    const CutRecord* rec = ws.cuts + blockIdx.x;
-    const int b = rec->b;
+    const CutRecord rec = ws.cuts[blockIdx.x];
+    const int b = rec.b;
     if (b < 0)
         return;
     const int in_slot = blockIdx.y * kMergeWaves + wave;   // w * cpw + column
     if (in_slot >= HG * cpw)
         return;
-    const int u = rec->u;
-    const int ncg = col_groups<MQ, NCT>(a, b);
-    const int hg = MQ ? u / ncg : u;
-    const int cg = MQ ? u - hg * ncg : 0;
+    const int u = rec.u;
+    const int hg = MQ ? u / rec.ncg : u;
+    const int cg = MQ ? u - hg * rec.ncg : 0;
     const int h = hg * HG + in_slot / cpw;
     const int cc = in_slot % cpw;
     size_t orow;
@@ -873,26 +934,15 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     } else {
         const int col = cg * kCols + cc;
         const int i = col / G;
-        const int qs = a.query_start[b];
-        if (i >= a.query_start[b + 1] - qs)
+        if (i >= rec.q)
             return;
-        orow = (size_t)(qs + i) * a.Hq + h * G + (col - i * G);
+        orow = (size_t)(rec.qs + i) * a.Hq + h * G + (col - i * G);
     }
     float* o = a.out + orow * D;
-    const int n = tiles_of(a.context_lens[b]);
-    const long long total = rec->total;
-    const long long ustart = rec->ustart;
-    const long long ulast = ustart + n - 1;
-    auto range_of = [&](long long x) {
-        long long r = (long long)((double)x * (double)R / (double)total);
-        while (r + 1 < R && range_start(r + 1, total, R) <= x)
-            ++r;
-        while (r > 0 && range_start(r, total, R) > x)
-            --r;
-        return r;
-    };
+    const long long total = rec.total;
+    const long long ustart = rec.ustart;
     const long long rf = blockIdx.x;
-    const long long rl = range_of(ulast);
+    const long long rl = rec.rl;
     const int rows_per_slot = HG * cpw;
     // Groups between rf and rl with an empty range (fewer tiles than
     // groups) hold no piece of this unit.
@@ -906,8 +956,8 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     const int p0 = lane / cols;
     const int c4 = lane % cols;
     // one online pass (running max, rescaled sums) over this lane's
-    // pieces, four pieces' loads in flight per step
-    constexpr int kBatch = 4;
+    // pieces, eight pieces' loads in flight per step
+    constexpr int kBatch = 8;
     float m = -__builtin_inff();
     float wsum = 0.f;
     f32x4 accv = {0.f, 0.f, 0.f, 0.f};

@@ -39,13 +39,15 @@ struct DecodeArgs {
     float scale_log2;     // softmax scale * log2(e)
 };
 
-// The unit a work-group starts but leaves unfinished (b < 0: none).
+// The unit a work-group starts but leaves unfinished (b < 0: none), with
+// everything its merge needs.
 struct CutRecord {
-    int32_t b;                // sequence
-    int32_t u;                // unit of the sequence (head group, column group)
     long long ustart;         // linear index of the unit's first tile
     long long total;          // tiles of the whole call
-    long long pad;
+    long long rl;             // work-group holding the unit's last tile
+    int32_t b, u;             // sequence, unit of the sequence (head group, column group)
+    int32_t n, ncg;           // tiles of the unit, column groups of the sequence
+    int32_t qs, q;            // several new tokens: first row and rows of the sequence
 };
 
 // Workspace of the balanced schedule: 2 partial slots per launched
