@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved KV-read GB/s (% of HBM peak) + decode tokens/s, paged decode attn 1 GPU"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0    # dense bf16
 
 DEFAULT_WORKLOAD = "llama70b_b64_ragged1k_16k_bs32"
 
@@ -241,6 +242,16 @@ def main():
     step_s = wall / a.steps
     gbs = ideal / step_s / 1e9
     kern_gbs = per_layer / kern_s / 1e9
+    # algorithmic flops of one attention call: q.k and p.v, 2 per multiply-add,
+    # per (row or sequence, query head, visible token, head-dim element)
+    if multi:
+        qn = mq.query_lens.astype(np.int64)
+        visible = int((qn * (ctx - qn) + qn * (qn + 1) // 2).sum())
+    else:
+        visible = int(ctx.sum())
+    flops = 4 * wl.Hq * wl.D * visible
+    mfma_bound = flops / per_layer > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    kern_tflops = flops / kern_s / 1e12
     traffic = _measured_traffic(a.traffic_json, f"{wl.name}:{mode}"
                                 + (f":{fmt}" if fmt != wl.kv_dtype else ""))
 
@@ -281,7 +292,13 @@ def main():
                      "multiquery": "paged_kv_write + paged_multiquery_attention (causal, "
                                    "log-sum-exp merge of cut units)"}[mode],
         },
-        "roofline": {
+        "roofline": ({
+            "bound": "mfma", "kernel": "prefill_kernel",
+            "achieved": round(kern_tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(kern_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+            "launch_us": round(kern_s * 1e6, 2), "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": per_layer,
+        } if mfma_bound else {
             "bound": "hbm",
             "kernel": {"split": "decode_kernel (split)", "single": "decode_kernel",
                        "balanced": "decode_balanced_kernel + balanced_merge_kernel",
@@ -290,7 +307,8 @@ def main():
             "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": per_layer,
-        },
+        }),
+        "attention_tflops": round(kern_tflops, 2),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

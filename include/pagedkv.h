@@ -298,7 +298,9 @@ int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows,
  * paged_kv_write of the same rows.  Scheduled like
  * paged_decode_attention_balanced: every sequence's tokens are streamed
  * once per kv head while its q_b * G (new row, query head) pairs are at
- * most 32, once per 32 pairs beyond that.
+ * most 32, once per 32 pairs up to 128; when max_query_len * G exceeds 128
+ * (prefill chunks) a work-group per 256 pairs stages each K/V tile in LDS
+ * for all of them (the workspace is then unused).
  *
  *  query          : [total_rows, Hq, D] bf16 bits (device, 16-byte aligned).
  *  query_start    : [B + 1] int32 (device); total_rows, max_query_len host.

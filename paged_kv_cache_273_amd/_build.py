@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SO = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["abi.hip", "decode.hip", "append_reduce.hip", "blocks.hip", "block_manager.cpp"]
+SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "append_reduce.hip", "blocks.hip",
+           "block_manager.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -385,6 +385,11 @@ int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows, const int32_t
     return launched(pkv::launch_write(a, (hipStream_t)stream));
 }
 
+// Beyond this many (new row, query head) columns per kv head the decode-
+// shaped multi-query path would stream each context more than four times;
+// the prefill kernel streams it once per 256 columns.
+constexpr int64_t kPrefillColumns = 128;
+
 // 16-column MFMA tiles per wave of the multi-query kernel: two once a kv
 // head has more than 16 (new row, query head) columns.
 static int mq_tiles_per_wave(int32_t max_query_len, int32_t G)
@@ -504,6 +509,9 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     if (max_tiles * ((int64_t)n + 1) >= ((int64_t)1 << 52))
         return PKV_EUNSUPPORTED;
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
+    if ((int64_t)max_query_len * G > kPrefillColumns)
+        return launched(pkv::launch_prefill(a, max_query_len, D, block_size, fmt.kvf, nt,
+                                            (hipStream_t)stream));
     return launched(pkv::launch_multiquery(a, ws, D, block_size, fmt.kvf, nct, nt,
                                            (hipStream_t)stream));
 }

@@ -121,6 +121,10 @@ hipError_t launch_move_blocks(const BlockMoveArgs& a, hipStream_t stream);
 // schedule; nct = 16-column MFMA tiles per wave (1 or 2).
 hipError_t launch_multiquery(const DecodeArgs& a, const BalanceArgs& ws, int D, int block_size,
                              int kv_dtype, int nct, bool nt, hipStream_t stream);
+// Long runs of new tokens: one work-group per 256 (row, head) columns of a
+// (sequence, kv head), K/V tiles shared through LDS; no workspace.
+hipError_t launch_prefill(const DecodeArgs& a, int max_query_len, int D, int block_size,
+                          int kvf, bool nt, hipStream_t stream);
 // resident work-groups per compute unit of the multi-query kernel (0 on error)
 int multiquery_groups_per_cu(int D, int block_size, int kv_dtype, int head_group, int nct);
 // kv heads per work-group of the balanced decode for Hkv kv heads

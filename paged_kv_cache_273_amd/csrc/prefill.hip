@@ -1,0 +1,390 @@
+// prefill.hip -- causal attention of long runs of new tokens (prefill
+// chunks) over a paged cache, for gfx950.
+//
+// Pages cited:
+//   [B] "KV Cache Engineering: PagedAttention, Continuous Batching,
+//        Attention Variants, and the Bandwidth Wall" -- "Continuous
+//        Batching" (chunked prefill), "PagedAttention", "Attention
+//        Variants" (GQA), "FP8 KV cache", "INT8 KV cache"
+//
+// Same operation as the multi-query path of decode.hip: row
+// query_start[b] + i of sequence b is position p = T_b - q_b + i and
+// attends over tokens [0, p] of kv head hq / G.  When a sequence brings
+// many new tokens, the (row, head) pairs of one kv head are many MFMA
+// columns, and giving every 32 of them their own pass over the context (as
+// the decode-shaped path does) would read the context once per 32 columns.
+// Here a work-group of 8 waves takes 256 columns of one (sequence, kv head)
+// and streams the context once for all of them: each 32-token tile of K and
+// V is loaded by the whole group, converted to bf16 and staged in LDS
+// (double-buffered, one barrier per tile); every wave then forms its two
+// 16-column score tiles from LDS K, runs the online softmax and
+// accumulates V^T . P^T from LDS V, exactly as the decode tile body does.
+// Work-groups that share a (sequence, kv head) are placed on one XCD so
+// their re-reads of the context hit that XCD's L2.
+//
+// fp8 codes become exact bf16 values in LDS and the block scales enter
+// through the scores (K) and probabilities (V); int8 codes become the
+// exact bf16 integers u - zp.
+#include "pkv_device.hpp"
+#include "pkv_kernels.hpp"
+
+namespace pkv {
+namespace {
+
+constexpr int kPWaves = 8;                         // waves per work-group
+constexpr int kPThreads = kPWaves * kWave;
+constexpr int kPCols = 32;                         // MFMA columns per wave
+constexpr int kPGroupCols = kPWaves * kPCols;      // columns per work-group
+constexpr int kPTile = 32;                         // tokens per staged tile
+constexpr int kXcds = 8;
+
+template <int D, int KVF>
+struct PCfg {
+    static constexpr int ESZ = KVF ? 1 : 2;
+    static constexpr int ROW_BYTES = D * ESZ;          // one cached token row
+    static constexpr int CPR = ROW_BYTES / 16;         // 16-byte chunks per row
+    static constexpr int NCHUNK = kPTile * CPR;        // chunks per K (or V) tile
+    static constexpr int CPT = (2 * NCHUNK + kPThreads - 1) / kPThreads;  // per thread
+    static constexpr int KPITCH = D * 2 + 16;          // bf16 K row pitch in LDS
+    static constexpr int VPITCH = D * 2 + 8;           // bf16 V row pitch in LDS
+    static constexpr int KBYTES = kPTile * KPITCH;
+    static constexpr int BUF = KBYTES + kPTile * VPITCH;
+    static constexpr int KSTEPS = D / 32;
+    static constexpr int DT = D / 16;
+};
+
+template <int NT>
+__device__ __forceinline__ u32x4 pload(const unsigned char* p)
+{
+    if (NT)
+        return __builtin_nontemporal_load((const u32x4*)p);
+    return *(const u32x4*)p;
+}
+
+// Token (of the 32-token tile) in contraction slot (q, i) of the PV product.
+__device__ __forceinline__ int ptoken(int q, int i)
+{
+    return i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4);
+}
+
+template <int D, int BS, int KVF, int NT>
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_t units,
+                                                            int32_t row_blocks)
+{
+    using C = PCfg<D, KVF>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // 2 tile buffers
+
+    // XCD-aware unit order: consecutive units (the row blocks of one
+    // sequence and kv head) run on one XCD.
+    const int per_xcd = (units + kXcds - 1) / kXcds;
+    const int unit = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (unit >= units || blockIdx.x / kXcds >= per_xcd)
+        return;
+    const int rb = unit % row_blocks;
+    const int bh = unit / row_blocks;
+    const int h = bh % a.Hkv;
+    const int b = bh / a.Hkv;
+    const int qs = a.query_start[b];
+    const int q = a.query_start[b + 1] - qs;
+    const int G = a.G;
+    if (rb * kPGroupCols >= q * G)
+        return;                                           // uniform over the group
+    const int T = a.context_lens[b];
+    const int tid = threadIdx.x;
+    const int lane = __lane_id();
+    const int q4 = lane >> 4;
+    const int r16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // this group's last row and its causal limit bound the token range
+    const int last_col = min(q * G, (rb + 1) * kPGroupCols) - 1;
+    const int t_end = T - q + last_col / G + 1;
+
+    // this lane's two columns
+    int lim[2], qrow[2], hq[2];
+    bool live[2];
+    bf16x8 qf[2][C::KSTEPS];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = rb * kPGroupCols + wave * kPCols + 16 * j + r16;
+        const int i = c / G;
+        live[j] = i < q;
+        qrow[j] = qs + (live[j] ? i : 0);
+        hq[j] = h * G + (c - i * G);
+        lim[j] = live[j] ? T - q + i + 1 : 0;
+        const uint16_t* qp = a.query + ((size_t)qrow[j] * a.Hq + (live[j] ? hq[j] : 0)) * D;
+#pragma unroll
+        for (int k = 0; k < C::KSTEPS; ++k) {
+            u32x4 v = *(const u32x4*)(qp + 8 * (q4 + 4 * k));
+            if (!live[j])
+                v = u32x4{0u, 0u, 0u, 0u};
+            qf[j][k] = as_bf16x8(v);
+        }
+    }
+    // wave-uniform bounds of the wave's columns
+    const int wc0 = rb * kPGroupCols + wave * kPCols;
+    const int w_first = min(wc0, q * G - 1) / G;
+    const int w_last = min(wc0 + kPCols, q * G) - 1;
+    const int wave_from = T - q + w_first + 1;           // no column's limit below
+    const int wave_end = wc0 < q * G ? T - q + w_last / G + 1 : 0;
+
+    const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
+    const unsigned char* kc = (const unsigned char*)a.k_cache;
+    const unsigned char* vc = (const unsigned char*)a.v_cache;
+    const size_t tok_stride = (size_t)a.Hkv * C::ROW_BYTES;
+    const size_t head_off = (size_t)h * C::ROW_BYTES;
+
+    auto scale_at = [&](const float* s, int p, int off) -> float {
+        return s[(size_t)p * a.sc_blk + (size_t)h * a.sc_head + off];
+    };
+
+    // cooperative load of one tile's chunks into registers
+    u32x4 reg[C::CPT];
+    auto fetch = [&](int t0) {
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            const int c = tid + u * kPThreads;
+            reg[u] = u32x4{0u, 0u, 0u, 0u};
+            if (c < 2 * C::NCHUNK) {
+                const int kv = c / C::NCHUNK;
+                const int rem = c - kv * C::NCHUNK;
+                const int row = rem / C::CPR;
+                const int col = rem - row * C::CPR;
+                const int t = t0 + row;
+                if (t < t_end) {
+                    const int p = trow[t / BS];
+                    const unsigned char* base = (kv ? vc : kc) + ((size_t)p * BS + t % BS) * tok_stride
+                                                + head_off + 16 * col;
+                    reg[u] = pload<NT>(base);
+                }
+            }
+        }
+    };
+    // registers -> bf16 rows of LDS buffer `buf`
+    auto stage = [&](int t0, int buf) {
+        unsigned char* kl = lds + buf * C::BUF;
+        unsigned char* vl = kl + C::KBYTES;
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            const int c = tid + u * kPThreads;
+            if (c >= 2 * C::NCHUNK)
+                continue;
+            const int kv = c / C::NCHUNK;
+            const int rem = c - kv * C::NCHUNK;
+            const int row = rem / C::CPR;
+            const int col = rem - row * C::CPR;
+            unsigned char* dst = kv ? vl + row * C::VPITCH : kl + row * C::KPITCH;
+            if (!KVF) {
+                u32x2* d2 = (u32x2*)(dst + 16 * col);
+                d2[0] = u32x2{reg[u][0], reg[u][1]};
+                d2[1] = u32x2{reg[u][2], reg[u][3]};
+            } else {
+                u32x4 lo, hi;
+                const int t = t0 + row;
+                if (KVF == 1) {
+                    fp8x16_to_bf16x16(reg[u], lo, hi);
+                } else {
+                    float zp = 0.f;
+                    if (t < t_end)
+                        zp = scale_at(kv ? a.v_scale : a.k_scale, trow[t / BS], 1);
+                    u8x16_to_bf16x16(reg[u], zp, lo, hi);
+                    if (t >= t_end) {
+                        lo = u32x4{0u, 0u, 0u, 0u};
+                        hi = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+                u32x2* d2 = (u32x2*)(dst + 32 * col);
+                d2[0] = u32x2{lo[0], lo[1]};
+                d2[1] = u32x2{lo[2], lo[3]};
+                d2[2] = u32x2{hi[0], hi[1]};
+                d2[3] = u32x2{hi[2], hi[3]};
+            }
+        }
+    };
+
+    f32x4 acc[2][C::DT];
+    float m_run[2], l_run[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+            acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[j] = -__builtin_inff();
+        l_run[j] = 0.f;
+    }
+    const float sl2 = a.scale_log2;
+
+    auto compute = [&](int t0, int buf) {
+        const unsigned char* kl = lds + buf * C::BUF;
+        const unsigned short* v16 = (const unsigned short*)(kl + C::KBYTES);
+        float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
+        if (KVF) {
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const int t = min(t0 + 16 * tau, t_end - 1);
+                const int p = trow[t / BS];
+                ks[tau] = scale_at(a.k_scale, p, 0);
+                vs[tau] = scale_at(a.v_scale, p, 0);
+            }
+        }
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            sacc[0][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sacc[1][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < C::KSTEPS; ++k) {
+                const u32x4 kw =
+                    *(const u32x4*)(kl + (16 * tau + r16) * C::KPITCH + 16 * (q4 + 4 * k));
+                sacc[0][tau] = mfma_16x16x32(as_bf16x8(kw), qf[0][k], sacc[0][tau]);
+                sacc[1][tau] = mfma_16x16x32(as_bf16x8(kw), qf[1][k], sacc[1][tau]);
+            }
+        }
+        const bool masked = t0 + kPTile > wave_from;
+        bf16x8 pb[2], pb_lo[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float s[8];
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const float f = KVF ? sl2 * ks[tau] : sl2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = sacc[j][tau][i] * f;
+                    if (masked && t0 + 16 * tau + 4 * q4 + i >= lim[j])
+                        x = -__builtin_inff();
+                    s[4 * tau + i] = x;
+                }
+            }
+            float mt = s[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                mt = fmaxf(mt, s[i]);
+            mt = fmaxf(mt, xor_shuffle(mt, 16));
+            mt = fmaxf(mt, xor_shuffle(mt, 32));
+            const float m_new = fmaxf(m_run[j], mt);
+            const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
+            m_run[j] = m_new;
+            float p[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+                psum += p[i];
+            }
+            l_run[j] = l_run[j] * alpha + psum;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                acc[j][dt] *= alpha;
+            if (KVF) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] *= vs[0];
+                    p[4 + i] *= vs[1];
+                }
+            }
+            // P as hi + lo bf16 terms (about 16 significant bits)
+            u32x4 pw, pr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pw[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+                pr[i] = pack_bf16x2(p[2 * i] - bf16_bits_to_f32(pw[i] & 0xFFFFu),
+                                    p[2 * i + 1] - bf16_bits_to_f32(pw[i] >> 16));
+            }
+            pb[j] = as_bf16x8(pw);
+            pb_lo[j] = as_bf16x8(pr);
+        }
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+            u32x4 vw;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t lo = v16[(ptoken(q4, i) * C::VPITCH) / 2 + 16 * dt + r16];
+                const uint32_t hi = v16[(ptoken(q4, i + 1) * C::VPITCH) / 2 + 16 * dt + r16];
+                vw[i / 2] = lo | (hi << 16);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                acc[j][dt] = mfma_16x16x32(as_bf16x8(vw), pb[j], acc[j][dt]);
+                acc[j][dt] = mfma_16x16x32(as_bf16x8(vw), pb_lo[j], acc[j][dt]);
+            }
+        }
+    };
+
+    // pipeline: the next tile's loads are in flight while this one is
+    // computed; one barrier per tile hands the buffers over
+    const int ntiles = (t_end + kPTile - 1) / kPTile;
+    fetch(0);
+    stage(0, 0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int t0 = it * kPTile;
+        const bool more = it + 1 < ntiles;
+        if (more)
+            fetch(t0 + kPTile);
+        if (t0 < wave_end)
+            compute(t0, it & 1);
+        if (more)
+            stage(t0 + kPTile, (it + 1) & 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float l = l_run[j];
+        l += xor_shuffle(l, 16);
+        l += xor_shuffle(l, 32);
+        if (!live[j])
+            continue;
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const size_t orow = (size_t)qrow[j] * a.Hq + hq[j];
+        float* o = a.out + orow * D;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+            *(f32x4*)(o + 16 * dt + 4 * q4) = acc[j][dt] * inv;
+        if (a.lse_out && q4 == 0)
+            a.lse_out[orow] = (m_run[j] + __builtin_log2f(l)) * kLn2;
+    }
+}
+
+template <int D, int BS, int KVF>
+hipError_t launch_prefill_t(const DecodeArgs& a, int max_query_len, bool nt, hipStream_t stream)
+{
+    const long long row_blocks =
+        ((long long)max_query_len * a.G + kPGroupCols - 1) / kPGroupCols;
+    const long long units = (long long)a.B * a.Hkv * row_blocks;
+    if (units <= 0)
+        return hipSuccess;
+    const long long groups = (units + kXcds - 1) / kXcds * kXcds;
+    if (groups > 0x7FFFFFFFLL)
+        return hipErrorInvalidConfiguration;
+    const size_t lds = 2 * (size_t)PCfg<D, KVF>::BUF;
+    if (nt)
+        hipLaunchKernelGGL((prefill_kernel<D, BS, KVF, 1>), dim3((unsigned)groups),
+                           dim3(kPThreads), lds, stream, a, (int32_t)units, (int32_t)row_blocks);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, BS, KVF, 0>), dim3((unsigned)groups),
+                           dim3(kPThreads), lds, stream, a, (int32_t)units, (int32_t)row_blocks);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_prefill(const DecodeArgs& a, int max_query_len, int D, int block_size,
+                          int kvf, bool nt, hipStream_t stream)
+{
+#define PKV_PF(d, bs)                                                                   \
+    if (D == d && block_size == bs)                                                    \
+        return kvf == 2   ? launch_prefill_t<d, bs, 2>(a, max_query_len, nt, stream)    \
+               : kvf == 1 ? launch_prefill_t<d, bs, 1>(a, max_query_len, nt, stream)    \
+                          : launch_prefill_t<d, bs, 0>(a, max_query_len, nt, stream);
+    PKV_PF(128, 16)
+    PKV_PF(128, 32)
+    PKV_PF(64, 16)
+    PKV_PF(64, 32)
+#undef PKV_PF
+    return hipErrorInvalidValue;
+}
+
+} // namespace pkv

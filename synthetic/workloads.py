@@ -155,6 +155,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("llama70b_b64_ragged1k_16k_bs32_verify4", B=64, Hq=64, Hkv=8, D=128,
                  block_size=32, max_blocks=512, ctx_uniform=(1024, 16384),
                  pool="holes10", q_uniform=(4, 4), seed=273002),
+        # chunked prefill: the last 512 tokens of 4 x 8192-token prompts are new
+        Workload("llama8b_b4_ctx8k_chunk512", B=4, Hq=32, Hkv=8, D=128, block_size=16,
+                 max_blocks=512, ctx_fixed=(8192,) * 4, pool="exact", q_uniform=(512, 512),
+                 seed=273005),
         # fp8 cache, 36 layers in 9 groups of 4 sharing one cache per group
         Workload("fp8_36layers_groups4_b32_ctx2k_8k", B=32, Hq=32, Hkv=4, D=128,
                  block_size=16, max_blocks=512, kv_dtype="fp8",

@@ -126,19 +126,24 @@ def test_write_is_bit_exact(orc, pkv, kv):
         assert np.array_equal(bits16(d.k), kp) and np.array_equal(bits16(d.v), vp)
 
 
+@pytest.mark.parametrize("runs", ["short", "long"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("G", [1, 4, 8, 16])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("D", [64, 128])
-def test_shapes(orc, pkv, D, bs, G, kv):
-    """Every kernel shape; q_b from 0 to T_b, so units span one to many
-    column groups and the causal edge falls at every offset of a tile."""
+def test_shapes(orc, pkv, D, bs, G, kv, runs):
+    """Every kernel shape; q_b from 0 to T_b, so the causal edge falls at
+    every offset of a tile.  "long" runs (up to 300 new tokens) take the
+    prefill kernel (256 columns per work-group, K/V staged in LDS); "short"
+    runs (q_b * G <= 128) the decode-shaped path with one to four column
+    groups per unit."""
     Hkv = 2
     wl = make_workload(TINY, B=len(EDGE_CTX), Hq=G * Hkv, Hkv=Hkv, D=D, block_size=bs,
                        ctx_fixed=EDGE_CTX, max_blocks=(300 + bs - 1) // bs + 1,
                        pool="holes10", kv_dtype=kv, seed=2200 + D + bs + G)
-    mq = generate_multiquery(wl, query_lens=np.array(Q_CYCLE))
-    print(f"mq shape D={D} bs={bs} G={G} kv={kv}", flush=True)
+    qlens = np.array(Q_CYCLE) if runs == "long" else np.minimum(np.array(Q_CYCLE), 128 // G)
+    mq = generate_multiquery(wl, query_lens=qlens)
+    print(f"mq shape D={D} bs={bs} G={G} kv={kv} runs={runs}", flush=True)
     if kv == "fp8":
         kc, vc, ks, vs = fp8_pools(orc, mq)
         d = MQDevice(mq, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
@@ -268,6 +273,48 @@ def test_verify4_fullsize_sampled(orc, pkv, kv):
     kp, vp = host_written(orc, mq, kc, vc, **kw)
     o, l = out.cpu().numpy(), lse.cpu().numpy()
     for (row, hq) in sample_rows(mq.rows, wl.Hq, 24, seed=5):
+        b = int(np.searchsorted(mq.query_start, row, side="right") - 1)
+        p = int(base.context_lens[b]) - int(mq.query_lens[b]) + (row - int(mq.query_start[b]))
+        ref, rl = orc.paged_attention(np.ascontiguousarray(mq.query[0][row:row + 1]), kp, vp,
+                                      np.ascontiguousarray(base.block_tables[b:b + 1]),
+                                      np.array([p + 1], dtype=np.int32), base.scale,
+                                      block_size=wl.block_size, Hkv=wl.Hkv, **kw)
+        assert_close(o[row, hq], ref[0, hq], f"row {row} head {hq}")
+        assert_close(l[row, hq], rl[0, hq], f"lse row {row} head {hq}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_prefill_chunk_sampled(orc, pkv, kv):
+    """A 700-token chunk at the end of 3000-token prompts (8B shape): the
+    prefill kernel, sampled rows against the oracle (row i is the decode
+    attention over the first T - 700 + i + 1 tokens)."""
+    wl = make_workload("llama8b_b4_ctx8k_chunk512", B=2, ctx_fixed=(3000, 2100),
+                       max_blocks=200, q_uniform=(700, 700), seed=2400)
+    mq = generate_multiquery(wl)
+    base = mq.base
+    print(f"prefill chunk kv={kv}", flush=True)
+    if kv == "int8":
+        ks = orc.int8_block_params(base.k_pool[0], base.block_tables, base.context_lens,
+                                   wl.block_size)
+        vs = orc.int8_block_params(base.v_pool[0], base.block_tables, base.context_lens,
+                                   wl.block_size)
+        kc, vc = orc.quantize_pool(base.k_pool[0], ks, "int8"), orc.quantize_pool(base.v_pool[0], vs,
+                                                                                    "int8")
+        kw = dict(kv_dtype="int8", k_scale=ks, v_scale=vs)
+        dkw = dict(kv_dtype="int8", k_scale=to_dev(ks), v_scale=to_dev(vs))
+    else:
+        kc, vc = base.k_pool[0], base.v_pool[0]
+        kw, dkw = {}, {}
+    d = MQDevice(mq, k_pool=kc, v_pool=vc)
+    pkv.paged_kv_write(d.k_rows, d.v_rows, d.qs, d.k, d.v, d.bt, d.cl, d.max_q, **dkw)
+    ws = pkv.make_multiquery_workspace(d.q, d.k, d.max_q, kv_dtype=dkw.get("kv_dtype"))
+    lse = torch.empty((mq.rows, wl.Hq), dtype=torch.float32, device=dev())
+    out = pkv.paged_multiquery_attention(d.q, d.qs, d.k, d.v, d.bt, d.cl, float(base.scale),
+                                         d.max_q, workspace=ws, lse_out=lse, **dkw)
+    torch.cuda.synchronize()
+    kp, vp = host_written(orc, mq, kc, vc, **kw)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for (row, hq) in sample_rows(mq.rows, wl.Hq, 32, seed=7):
         b = int(np.searchsorted(mq.query_start, row, side="right") - 1)
         p = int(base.context_lens[b]) - int(mq.query_lens[b]) + (row - int(mq.query_start[b]))
         ref, rl = orc.paged_attention(np.ascontiguousarray(mq.query[0][row:row + 1]), kp, vp,
