@@ -16,9 +16,10 @@
 // Here a work-group of 8 waves takes 256 columns of one (sequence, kv head)
 // and streams the context once for all of them: each 32-token tile of K and
 // V is loaded by the whole group, converted to bf16 and staged in LDS
-// (double-buffered, one barrier per tile); every wave then forms its two
-// 16-column score tiles from LDS K, runs the online softmax and
-// accumulates V^T . P^T from LDS V, exactly as the decode tile body does.
+// (double-buffered, one barrier per tile) -- V already transposed, so a
+// lane fetches its 8 PV contraction tokens with two 8-byte reads; every
+// wave then forms its two 16-column score tiles from LDS K, runs the online
+// softmax and accumulates V^T . P^T, as the decode tile body does.
 // Work-groups that share a (sequence, kv head) are placed on one XCD so
 // their re-reads of the context hit that XCD's L2.
 //
@@ -46,9 +47,9 @@ struct PCfg {
     static constexpr int NCHUNK = kPTile * CPR;        // chunks per K (or V) tile
     static constexpr int CPT = (2 * NCHUNK + kPThreads - 1) / kPThreads;  // per thread
     static constexpr int KPITCH = D * 2 + 16;          // bf16 K row pitch in LDS
-    static constexpr int VPITCH = D * 2 + 8;           // bf16 V row pitch in LDS
+    static constexpr int VTPITCH = kPTile * 2 + 8;     // bf16 V^T row (one head-dim element)
     static constexpr int KBYTES = kPTile * KPITCH;
-    static constexpr int BUF = KBYTES + kPTile * VPITCH;
+    static constexpr int BUF = KBYTES + D * VTPITCH;
     static constexpr int KSTEPS = D / 32;
     static constexpr int DT = D / 16;
 };
@@ -61,11 +62,6 @@ __device__ __forceinline__ u32x4 pload(const unsigned char* p)
     return *(const u32x4*)p;
 }
 
-// Token (of the 32-token tile) in contraction slot (q, i) of the PV product.
-__device__ __forceinline__ int ptoken(int q, int i)
-{
-    return i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4);
-}
 
 template <int D, int BS, int KVF, int NT>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_t units,
@@ -173,11 +169,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
             const int rem = c - kv * C::NCHUNK;
             const int row = rem / C::CPR;
             const int col = rem - row * C::CPR;
-            unsigned char* dst = kv ? vl + row * C::VPITCH : kl + row * C::KPITCH;
+            unsigned char* dst = kl + row * C::KPITCH;
+            // V^T: element d of token `row` at vl + d * VTPITCH + 2 * row
+            auto put_vt = [&](int d0, const u32x4& w) {
+                unsigned short* vt = (unsigned short*)(vl + d0 * C::VTPITCH) + row;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    vt[e * (C::VTPITCH / 2)] = (unsigned short)(w[e / 2] >> (16 * (e & 1)));
+            };
             if (!KVF) {
-                u32x2* d2 = (u32x2*)(dst + 16 * col);
-                d2[0] = u32x2{reg[u][0], reg[u][1]};
-                d2[1] = u32x2{reg[u][2], reg[u][3]};
+                if (kv) {
+                    put_vt(8 * col, reg[u]);
+                } else {
+                    u32x2* d2 = (u32x2*)(dst + 16 * col);
+                    d2[0] = u32x2{reg[u][0], reg[u][1]};
+                    d2[1] = u32x2{reg[u][2], reg[u][3]};
+                }
             } else {
                 u32x4 lo, hi;
                 const int t = t0 + row;
@@ -193,11 +200,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
                         hi = u32x4{0u, 0u, 0u, 0u};
                     }
                 }
-                u32x2* d2 = (u32x2*)(dst + 32 * col);
-                d2[0] = u32x2{lo[0], lo[1]};
-                d2[1] = u32x2{lo[2], lo[3]};
-                d2[2] = u32x2{hi[0], hi[1]};
-                d2[3] = u32x2{hi[2], hi[3]};
+                if (kv) {
+                    put_vt(16 * col, lo);
+                    put_vt(16 * col + 8, hi);
+                } else {
+                    u32x2* d2 = (u32x2*)(dst + 32 * col);
+                    d2[0] = u32x2{lo[0], lo[1]};
+                    d2[1] = u32x2{lo[2], lo[3]};
+                    d2[2] = u32x2{hi[0], hi[1]};
+                    d2[3] = u32x2{hi[2], hi[3]};
+                }
             }
         }
     };
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
 
     auto compute = [&](int t0, int buf) {
         const unsigned char* kl = lds + buf * C::BUF;
-        const unsigned short* v16 = (const unsigned short*)(kl + C::KBYTES);
+        const unsigned char* vt = kl + C::KBYTES;
         float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
         if (KVF) {
 #pragma unroll
@@ -274,9 +286,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
                 psum += p[i];
             }
             l_run[j] = l_run[j] * alpha + psum;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {     // a running max moved
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-                acc[j][dt] *= alpha;
+                for (int dt = 0; dt < C::DT; ++dt)
+                    acc[j][dt] *= alpha;
+            }
             if (KVF) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -297,13 +311,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-            u32x4 vw;
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const uint32_t lo = v16[(ptoken(q4, i) * C::VPITCH) / 2 + 16 * dt + r16];
-                const uint32_t hi = v16[(ptoken(q4, i + 1) * C::VPITCH) / 2 + 16 * dt + r16];
-                vw[i / 2] = lo | (hi << 16);
-            }
+            // contraction slots (q4, 0..3) = tokens 4q4.., (q4, 4..7) = 16 + 4q4..
+            const unsigned char* row = vt + (16 * dt + r16) * C::VTPITCH;
+            const u32x2 a0 = *(const u32x2*)(row + 8 * q4);
+            const u32x2 a1 = *(const u32x2*)(row + 32 + 8 * q4);
+            const u32x4 vw = {a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 acc[j][dt] = mfma_16x16x32(as_bf16x8(vw), pb[j], acc[j][dt]);
