@@ -17,11 +17,12 @@
  *    patterns.  `stream` is a hipStream_t passed as void* (NULL = the
  *    default stream).
  *  * Ownership: the caller owns and allocates everything (pools, scales,
- *    tables, lengths, partials, outputs).  The library allocates nothing,
- *    frees nothing, never synchronises and keeps no state between calls;
- *    each call only enqueues kernels on `stream` and returns (the balanced
- *    decode also reads the current device's compute-unit count).  Calls
- *    are thread-safe.
+ *    tables, lengths, partials, outputs).  The library allocates no device
+ *    memory, frees nothing and never synchronises; each call only enqueues
+ *    kernels on `stream` and returns.  The balanced schedules read the
+ *    current device's compute-unit count and kernel occupancy once per
+ *    device and configuration and keep them in a small host-side table
+ *    (the only state between calls).  Calls are thread-safe.
  *  * Errors: scalar arguments and pointer alignment are checked on the
  *    host before anything is launched.  A bad argument returns
  *    PKV_EINVAL, a shape outside the compiled kernel set returns

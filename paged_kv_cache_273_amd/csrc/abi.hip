@@ -1,8 +1,13 @@
 // abi.hip -- the C ABI of libpagedkv.so (declared in include/pagedkv.h).
 // Host-side argument checks, then one launch on the caller's stream.
-// Nothing here allocates, frees or synchronises.
+// Nothing here allocates device memory, frees or synchronises (a small
+// host-side table caches the resident work-group count per device and
+// kernel configuration).
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
+#include <unordered_map>
 
 #include "../../include/pagedkv.h"
 #include "pkv_kernels.hpp"
@@ -211,15 +216,44 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
 
 // Work-groups of the balanced decode on the current device: exactly the
 // number that can be resident at once, so every group starts immediately.
-static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype)
+// Resident work-groups of one balanced-schedule kernel configuration on
+// the current device (compute units x groups per CU), cached per device:
+// the occupancy query is host work every call would otherwise repeat.
+// nct = 0 selects the decode kernel, 1 or 2 the multi-query kernel.
+static int resident_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype,
+                           int nct)
 {
-    int dev = 0, cus = 0;
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return 0;
+    const int kvf = format_of(kv_dtype, Hkv).kvf;
+    const int hg = pkv::balanced_head_group(Hkv);
+    const uint64_t key = ((((((uint64_t)dev * 256 + D) * 64 + block_size) * 4 + kvf) * 16 + hg)
+                          * 4 + nct);
+    static std::mutex mu;
+    static std::unordered_map<uint64_t, int> cache;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        auto it = cache.find(key);
+        if (it != cache.end())
+            return it->second;
+    }
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    const int hg = pkv::balanced_head_group(Hkv);
-    return cus * pkv::balanced_groups_per_cu(D, block_size, format_of(kv_dtype, Hkv).kvf, hg);
+    const int per_cu = nct == 0 ? pkv::balanced_groups_per_cu(D, block_size, kvf, hg)
+                                : pkv::multiquery_groups_per_cu(D, block_size, kvf, hg, nct);
+    const int n = cus * per_cu;
+    if (n > 0) {
+        std::lock_guard<std::mutex> g(mu);
+        cache.emplace(key, n);
+    }
+    return n;
+}
+
+static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype)
+{
+    return resident_groups(Hkv, D, block_size, kv_dtype, 0);
 }
 
 // Partial slots (2 per work-group) of rows_per_group rows, then the cut
@@ -399,14 +433,7 @@ static int mq_tiles_per_wave(int32_t max_query_len, int32_t G)
 
 static int mq_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtype, int nct)
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    const int hg = pkv::balanced_head_group(Hkv);
-    return cus * pkv::multiquery_groups_per_cu(D, block_size, format_of(kv_dtype, Hkv).kvf, hg,
-                                                nct);
+    return resident_groups(Hkv, D, block_size, kv_dtype, nct);
 }
 
 static int64_t mq_bytes(int ngroups, int32_t Hkv, int nct, int32_t D)
