@@ -13,9 +13,9 @@ already resident in HBM.
 
 Prints ONE JSON line.  value = KV-read GB/s of the whole step (ideal KV
 bytes 2 * sum(ctx) * Hkv * D * bytes_per_elem per layer call, times the
-layers, / step time).  roofline = one attention call per step (layer
-i mod layers in step i), timed with HIP events on the stream it is
-launched on.  cpu_baseline = the CPU oracle on a bounded sample of the
+layers, / step time).  roofline = the attention call of every 8th timed
+step (layer i mod layers in step i), timed with HIP events on the stream
+it is launched on.  cpu_baseline = the CPU oracle on a bounded sample of the
 same workload, on this machine's host cores.
 """
 from __future__ import annotations
@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved KV-read GB/s (% of HBM peak) + decode tokens/s, paged decode attn 1 GPU"
 HBM_PEAK_GBS = 8000.0
+EVENT_STRIDE = 8             # timed steps per sampled attention launch
 MFMA_PEAK_TFLOPS = 2500.0    # dense bf16
 
 DEFAULT_WORKLOAD = "llama70b_b64_ragged1k_16k_bs32"
@@ -60,6 +61,9 @@ def _args():
     p.add_argument("--preempt", type=int, default=8,
                    help="sequences swapped out and back in (--mode swap)")
     p.add_argument("--split", type=int, default=None, help="split_tokens for --mode split")
+    p.add_argument("--unfused", action="store_true",
+                   help="append with paged_kv_append in its own launch instead of inside "
+                        "the attention launch of each cache group's first layer")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -181,34 +185,54 @@ def main():
     if mode == "multiquery":
         ws = pkv.make_multiquery_workspace(qs[0], caches[0][0], max_q, kv_dtype=fmt)
 
-    # (start, end) HIP events around one attention call per timed step: layer
-    # i % layers in step i, so every layer's call is sampled without putting
-    # two event records around each of the step's calls
+    # (start, end) HIP events around one attention call of every
+    # EVENT_STRIDE-th timed step (layer i % layers in step i, so every
+    # layer's call is sampled).  An event pair costs ~6 us of GPU time (two
+    # marker packets); recorded in every step it would be charged to every
+    # step, ~6% of a 90 us step.
     ev = []
+
+    # decode steps append in the attention launch of each group's first
+    # layer (paged_append_decode_attention*), unless --unfused
+    fused = not multi and not a.unfused
 
     def step(record):
         for k, v, ks, vs, kn, vn in caches:
             if multi:
                 pkv.paged_kv_write(kn, vn, qstart, k, v, bt, cl, max_q, k_scale=ks, v_scale=vs,
                                    kv_dtype=fmt)
-            else:
+            elif not fused:
                 pkv.paged_kv_append(kn, vn, k, v, bt, cl, k_scale=ks, v_scale=vs, kv_dtype=fmt)
         for layer in range(wl.layers):
-            k, v, ks, vs, _, _ = caches[layer // wl.layers_per_group]
+            k, v, ks, vs, kn, vn = caches[layer // wl.layers_per_group]
             q = qs[layer]
-            timed = record is not None and layer == record % wl.layers
+            new = fused and layer % wl.layers_per_group == 0
+            timed = (record is not None and record % EVENT_STRIDE == 0
+                     and layer == record % wl.layers)
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            if mode == "split":
+            if mode == "split" and new:
+                pkv.paged_append_decode_attention(q, kn, vn, k, v, bt, cl, scale,
+                                                  split_tokens=S, partial_out=po,
+                                                  partial_lse=pl, k_scale=ks, v_scale=vs,
+                                                  kv_dtype=fmt)
+            elif mode == "split":
                 pkv.paged_decode_attention(q, k, v, bt, cl, scale, split_tokens=S,
                                            partial_out=po, partial_lse=pl, k_scale=ks,
                                            v_scale=vs, kv_dtype=fmt)
+            elif mode == "balanced" and new:
+                pkv.paged_append_decode_attention_balanced(q, kn, vn, k, v, bt, cl, scale,
+                                                           workspace=ws, out=out, k_scale=ks,
+                                                           v_scale=vs, kv_dtype=fmt)
             elif mode == "balanced":
                 pkv.paged_decode_attention_balanced(q, k, v, bt, cl, scale, workspace=ws,
                                                     out=out, k_scale=ks, v_scale=vs,
                                                     kv_dtype=fmt)
+            elif mode == "single" and new:
+                pkv.paged_append_decode_attention(q, kn, vn, k, v, bt, cl, scale, out=out,
+                                                  k_scale=ks, v_scale=vs, kv_dtype=fmt)
             elif mode == "multiquery":
                 pkv.paged_multiquery_attention(q, qstart, k, v, bt, cl, scale, max_q,
                                                workspace=ws, out=out, k_scale=ks, v_scale=vs,
@@ -284,13 +308,17 @@ def main():
             "layers_per_step": wl.layers, "cache_groups": wl.groups,
             "new_tokens_per_sequence": (list(wl.q_uniform) if multi else 1),
             "new_tokens_per_step": rows,
-            "step": {"split": "paged_kv_append + paged_decode_attention(split) + "
+            "step": ({"split": "paged_append_decode_attention(split) + split_context_reduce",
+                      "balanced": "paged_append_decode_attention_balanced (append + decode, "
+                                  "then log-sum-exp merge of cut units)",
+                      "single": "paged_append_decode_attention"} if fused else {
+                     "split": "paged_kv_append + paged_decode_attention(split) + "
                               "split_context_reduce",
                      "balanced": "paged_kv_append + paged_decode_attention_balanced "
                                  "(decode + log-sum-exp merge of cut units)",
                      "single": "paged_kv_append + paged_decode_attention",
                      "multiquery": "paged_kv_write + paged_multiquery_attention (causal, "
-                                   "log-sum-exp merge of cut units)"}[mode],
+                                   "log-sum-exp merge of cut units)"})[mode],
         },
         "roofline": ({
             "bound": "mfma", "kernel": "prefill_kernel",

@@ -243,6 +243,54 @@ int paged_decode_attention_balanced(const uint16_t* query,
                                     float* out, float* lse_out, void* stream);
 
 /*
+ * paged_append_decode_attention, paged_append_decode_attention_balanced --
+ * one decode step's append and attention in one launch: exactly
+ * paged_kv_append(k_new, v_new, ...) followed on the same stream by
+ * paged_decode_attention / paged_decode_attention_balanced with the same
+ * arguments ([B] "What the KV Cache Stores and Why": the step stores the
+ * new token's K and V, then its query attends over every cached token,
+ * the new one included).  The wave that attends a sequence's last
+ * position writes that position's row first, so the caches are both
+ * written and read by the call.
+ *
+ *  k_new, v_new   : [B, Hkv, D] bf16 bits (device), 16-byte aligned, as in
+ *                   paged_kv_append (same encoding for 1-byte formats, with
+ *                   the block's existing scale).
+ *  k_cache, v_cache : written at slot T_b - 1 of every sequence with
+ *                   T_b > 0, read everywhere else as in the attention call.
+ *  Other arguments, outputs, alignment and errors as in the attention call
+ *  (PKV_EINVAL also for a missing k_new / v_new).  The written slot must
+ *  belong to its sequence alone: a physical block shared with another
+ *  sequence of the batch (prefix sharing) is copied before its first
+ *  append (copy-on-write), as for paged_kv_append.
+ */
+int paged_append_decode_attention(const uint16_t* query,
+                                  const uint16_t* k_new, const uint16_t* v_new,
+                                  void* k_cache, void* v_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_tables, int32_t max_blocks,
+                                  const int32_t* context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t block_size, int32_t num_blocks,
+                                  int32_t kv_dtype, float scale,
+                                  int32_t split_tokens,
+                                  float* out,
+                                  float* partial_out, float* partial_lse,
+                                  int32_t max_splits, float* lse_out, void* stream);
+
+int paged_append_decode_attention_balanced(const uint16_t* query,
+                                           const uint16_t* k_new, const uint16_t* v_new,
+                                           void* k_cache, void* v_cache,
+                                           const float* k_scale, const float* v_scale,
+                                           const int32_t* block_tables, int32_t max_blocks,
+                                           const int32_t* context_lens,
+                                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                           int32_t block_size, int32_t num_blocks,
+                                           int32_t kv_dtype, float scale,
+                                           void* workspace, int64_t workspace_bytes,
+                                           float* out, float* lse_out, void* stream);
+
+/*
  * Bytes of workspace paged_decode_attention_balanced needs for these
  * head counts and cache format on the current device (it depends on the
  * device's compute-unit count), or a negative pkv_status.  Independent of

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
                                   its block-table-gathered cache
     split_context_reduce(...)     log-sum-exp merge of split-context partials
     paged_decode_attention_balanced(...)  the decode attention, work-balanced
+    paged_append_decode_attention(...), paged_append_decode_attention_balanced(...)
+                                  append and decode attention in one launch
     paged_kv_write(...)           several new K/V rows per sequence
     paged_multiquery_attention(...)  causal attention of several new tokens
 """
@@ -32,6 +34,7 @@ KV_DTYPES = {"bf16": PKV_BF16, "fp8": PKV_FP8_E4M3, "fp8_head": PKV_FP8_E4M3_PER
 
 EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "paged_decode_attention_balanced", "paged_decode_workspace_size",
+           "paged_append_decode_attention", "paged_append_decode_attention_balanced",
            "paged_kv_write", "paged_multiquery_attention", "paged_multiquery_workspace_size",
            "pkv_status_string", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
            "paged_kv_copy_blocks",
@@ -60,11 +63,16 @@ def _load(path=LIB_PATH):
     L.paged_decode_attention.restype = C.c_int
     L.paged_decode_attention.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, C.c_float,
                                          I, P, P, P, I, P, P]
+    L.paged_append_decode_attention.restype = C.c_int
+    L.paged_append_decode_attention.argtypes = [P, P, P] + L.paged_decode_attention.argtypes[1:]
     L.split_context_reduce.restype = C.c_int
     L.split_context_reduce.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
     L.paged_decode_attention_balanced.restype = C.c_int
     L.paged_decode_attention_balanced.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I,
                                                   C.c_float, P, C.c_int64, P, P, P]
+    L.paged_append_decode_attention_balanced.restype = C.c_int
+    L.paged_append_decode_attention_balanced.argtypes = (
+        [P, P, P] + L.paged_decode_attention_balanced.argtypes[1:])
     L.paged_decode_workspace_size.restype = C.c_int64
     L.paged_decode_workspace_size.argtypes = [I, I, I, I, I]
     L.paged_kv_write.restype = C.c_int
@@ -157,14 +165,8 @@ def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, 
     _check("paged_kv_append", st)
 
 
-def paged_decode_attention(query, k_cache, v_cache, block_tables, context_lens, scale, *,
-                           out=None, lse_out=None, split_tokens=0, partial_out=None,
-                           partial_lse=None, k_scale=None, v_scale=None, kv_dtype=None,
-                           stream=None):
-    """query [B, Hq, D] bf16.  split_tokens == 0: writes out [B, Hq, D] float32
-    (and lse_out [B, Hq]) and returns out.  split_tokens > 0: writes
-    partial_out [B, Hq, max_splits, D] / partial_lse [B, Hq, max_splits] and
-    returns them (combine with split_context_reduce)."""
+def _decode(name, query, new, k_cache, v_cache, block_tables, context_lens, scale, out,
+            lse_out, split_tokens, partial_out, partial_lse, k_scale, v_scale, kv_dtype, stream):
     _need(query, _BF16_BITS, "query")
     _need(block_tables, (torch.int32,), "block_tables")
     _need(context_lens, (torch.int32,), "context_lens")
@@ -181,13 +183,47 @@ def paged_decode_attention(query, k_cache, v_cache, block_tables, context_lens, 
         _need(partial_out, (torch.float32,), "partial_out")
         _need(partial_lse, (torch.float32,), "partial_lse")
         max_splits = partial_out.shape[2]
-    st = _lib.paged_decode_attention(
-        _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, nb,
-        _kv_dtype(k_cache, kv_dtype), float(scale), int(split_tokens), _ptr(out), _ptr(partial_out),
-        _ptr(partial_lse), max_splits, _ptr(lse_out), _stream(stream))
-    _check("paged_decode_attention", st)
+    st = getattr(_lib, name)(
+        _ptr(query), *_new_rows(new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq,
+        Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), float(scale), int(split_tokens),
+        _ptr(out), _ptr(partial_out), _ptr(partial_lse), max_splits, _ptr(lse_out),
+        _stream(stream))
+    _check(name, st)
     return out if split_tokens == 0 else (partial_out, partial_lse)
+
+
+def _new_rows(new):
+    if new is None:
+        return ()
+    k_new, v_new = new
+    _need(k_new, _BF16_BITS, "k_new")
+    _need(v_new, _BF16_BITS, "v_new")
+    return (_ptr(k_new), _ptr(v_new))
+
+
+def paged_decode_attention(query, k_cache, v_cache, block_tables, context_lens, scale, *,
+                           out=None, lse_out=None, split_tokens=0, partial_out=None,
+                           partial_lse=None, k_scale=None, v_scale=None, kv_dtype=None,
+                           stream=None):
+    """query [B, Hq, D] bf16.  split_tokens == 0: writes out [B, Hq, D] float32
+    (and lse_out [B, Hq]) and returns out.  split_tokens > 0: writes
+    partial_out [B, Hq, max_splits, D] / partial_lse [B, Hq, max_splits] and
+    returns them (combine with split_context_reduce)."""
+    return _decode("paged_decode_attention", query, None, k_cache, v_cache, block_tables,
+                   context_lens, scale, out, lse_out, split_tokens, partial_out, partial_lse,
+                   k_scale, v_scale, kv_dtype, stream)
+
+
+def paged_append_decode_attention(query, k_new, v_new, k_cache, v_cache, block_tables,
+                                  context_lens, scale, *, out=None, lse_out=None,
+                                  split_tokens=0, partial_out=None, partial_lse=None,
+                                  k_scale=None, v_scale=None, kv_dtype=None, stream=None):
+    """paged_kv_append(k_new, v_new, ...) then paged_decode_attention(...),
+    in one launch; k_new / v_new [B, Hkv, D] bf16."""
+    return _decode("paged_append_decode_attention", query, (k_new, v_new), k_cache, v_cache,
+                   block_tables, context_lens, scale, out, lse_out, split_tokens, partial_out,
+                   partial_lse, k_scale, v_scale, kv_dtype, stream)
 
 
 def paged_decode_workspace_size(Hq, Hkv, D, block_size, kv_dtype=PKV_BF16) -> int:
@@ -207,12 +243,8 @@ def make_workspace(query, k_cache, kv_dtype=None) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=query.device)
 
 
-def paged_decode_attention_balanced(query, k_cache, v_cache, block_tables, context_lens, scale,
-                                    *, workspace, out=None, lse_out=None, k_scale=None,
-                                    v_scale=None, kv_dtype=None, stream=None):
-    """Single-pass paged decode attention with the work of all (sequence,
-    kv head) pairs cut into equal ranges (for ragged batches).  workspace:
-    a device buffer of paged_decode_workspace_size(...) bytes."""
+def _balanced(name, query, new, k_cache, v_cache, block_tables, context_lens, scale, workspace,
+              out, lse_out, k_scale, v_scale, kv_dtype, stream):
     _need(query, _BF16_BITS, "query")
     _need(block_tables, (torch.int32,), "block_tables")
     _need(context_lens, (torch.int32,), "context_lens")
@@ -222,13 +254,35 @@ def paged_decode_attention_balanced(query, k_cache, v_cache, block_tables, conte
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
     _need(out, (torch.float32,), "out")
     nbytes = workspace.numel() * workspace.element_size()
-    st = _lib.paged_decode_attention_balanced(
-        _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, nb,
-        _kv_dtype(k_cache, kv_dtype), float(scale), _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out),
-        _stream(stream))
-    _check("paged_decode_attention_balanced", st)
+    st = getattr(_lib, name)(
+        _ptr(query), *_new_rows(new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq,
+        Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), float(scale), _ptr(workspace), nbytes,
+        _ptr(out), _ptr(lse_out), _stream(stream))
+    _check(name, st)
     return out
+
+
+def paged_decode_attention_balanced(query, k_cache, v_cache, block_tables, context_lens, scale,
+                                    *, workspace, out=None, lse_out=None, k_scale=None,
+                                    v_scale=None, kv_dtype=None, stream=None):
+    """Single-pass paged decode attention with the work of all (sequence,
+    kv head) pairs cut into equal ranges (for ragged batches).  workspace:
+    a device buffer of paged_decode_workspace_size(...) bytes."""
+    return _balanced("paged_decode_attention_balanced", query, None, k_cache, v_cache,
+                     block_tables, context_lens, scale, workspace, out, lse_out, k_scale,
+                     v_scale, kv_dtype, stream)
+
+
+def paged_append_decode_attention_balanced(query, k_new, v_new, k_cache, v_cache,
+                                           block_tables, context_lens, scale, *, workspace,
+                                           out=None, lse_out=None, k_scale=None,
+                                           v_scale=None, kv_dtype=None, stream=None):
+    """paged_kv_append(k_new, v_new, ...) then
+    paged_decode_attention_balanced(...), in one launch."""
+    return _balanced("paged_append_decode_attention_balanced", query, (k_new, v_new), k_cache,
+                     v_cache, block_tables, context_lens, scale, workspace, out, lse_out,
+                     k_scale, v_scale, kv_dtype, stream)
 
 
 def split_context_reduce(partial_out, partial_lse, context_lens, split_tokens, *, out=None,

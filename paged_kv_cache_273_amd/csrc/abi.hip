@@ -72,7 +72,6 @@ constexpr int32_t kMaxGroup = 16;     // query heads per kv head (one MFMA colum
 // MI355X last-level (Infinity Cache / MALL) capacity.  A K+V pool that fits
 // may be re-read from it by the next call; larger pools are streamed.
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
-constexpr int32_t kMaxSplits = 15360; // reduce keeps one weight per split in LDS
 // per-sequence token bound of the balanced path (64-sequence tile sums stay in int32)
 constexpr int64_t kMaxTokens = (int64_t)1 << 25;
 
@@ -151,13 +150,15 @@ int paged_kv_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache,
     return launched(pkv::launch_append(a, (hipStream_t)stream));
 }
 
-int paged_decode_attention(const uint16_t* query, const void* k_cache, const void* v_cache,
-                           const float* k_scale, const float* v_scale,
-                           const int32_t* block_tables, int32_t max_blocks,
-                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                           int32_t D, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
-                           float scale, int32_t split_tokens, float* out, float* partial_out,
-                           float* partial_lse, int32_t max_splits, float* lse_out, void* stream)
+// Decode attention on the fixed partition; with k_new / v_new the launch
+// also appends the step's new rows (paged_append_decode_attention).
+static int decode_call(const uint16_t* query, const uint16_t* k_new, const uint16_t* v_new,
+                       const void* k_cache, const void* v_cache, const float* k_scale,
+                       const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                       float scale, int32_t split_tokens, float* out, float* partial_out,
+                       float* partial_lse, int32_t max_splits, float* lse_out, void* stream)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0
         || max_blocks <= 0 || split_tokens < 0)
@@ -177,6 +178,8 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
         return PKV_EINVAL;
     if (one_byte(kv_dtype) && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    if (k_new && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
         return PKV_EINVAL;
     if (split_tokens == 0) {
         if (!out || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
@@ -210,8 +213,43 @@ int paged_decode_attention(const uint16_t* query, const void* k_cache, const voi
     const Fmt fmt = format_of(kv_dtype, Hkv);
     a.sc_blk = fmt.sc_blk;
     a.sc_head = fmt.sc_head;
+    a.k_new = k_new;
+    a.v_new = v_new;
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
     return launched(pkv::launch_decode(a, D, block_size, fmt.kvf, nt, (hipStream_t)stream));
+}
+
+int paged_decode_attention(const uint16_t* query, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                           float scale, int32_t split_tokens, float* out, float* partial_out,
+                           float* partial_lse, int32_t max_splits, float* lse_out, void* stream)
+{
+    return decode_call(query, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                       block_tables, max_blocks, context_lens, B, Hq, Hkv, D, block_size,
+                       num_blocks, kv_dtype, scale, split_tokens, out, partial_out,
+                       partial_lse, max_splits, lse_out, stream);
+}
+
+int paged_append_decode_attention(const uint16_t* query, const uint16_t* k_new,
+                                  const uint16_t* v_new, void* k_cache, void* v_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_tables, int32_t max_blocks,
+                                  const int32_t* context_lens, int32_t B, int32_t Hq,
+                                  int32_t Hkv, int32_t D, int32_t block_size,
+                                  int32_t num_blocks, int32_t kv_dtype, float scale,
+                                  int32_t split_tokens, float* out, float* partial_out,
+                                  float* partial_lse, int32_t max_splits, float* lse_out,
+                                  void* stream)
+{
+    if (B > 0 && (!k_new || !v_new))
+        return PKV_EINVAL;
+    return decode_call(query, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       max_blocks, context_lens, B, Hq, Hkv, D, block_size, num_blocks,
+                       kv_dtype, scale, split_tokens, out, partial_out, partial_lse,
+                       max_splits, lse_out, stream);
 }
 
 // Work-groups of the balanced decode on the current device: exactly the
@@ -295,14 +333,15 @@ int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t 
     return balanced_bytes(n, Hkv, Hq / Hkv, D);
 }
 
-int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
-                                    const void* v_cache, const float* k_scale,
-                                    const float* v_scale, const int32_t* block_tables,
-                                    int32_t max_blocks, const int32_t* context_lens, int32_t B,
-                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
-                                    int32_t num_blocks, int32_t kv_dtype, float scale,
-                                    void* workspace, int64_t workspace_bytes, float* out,
-                                    float* lse_out, void* stream)
+// Decode attention on the balanced schedule; with k_new / v_new the launch
+// also appends the step's new rows (paged_append_decode_attention_balanced).
+static int balanced_call(const uint16_t* query, const uint16_t* k_new, const uint16_t* v_new,
+                         const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                         float scale, void* workspace, int64_t workspace_bytes, float* out,
+                         float* lse_out, void* stream)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0
         || max_blocks <= 0 || workspace_bytes < 0)
@@ -323,6 +362,8 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
         || !aligned(out, 16) || !aligned(workspace, 16))
         return PKV_EINVAL;
     if (one_byte(kv_dtype) && (!k_scale || !v_scale))
+        return PKV_EINVAL;
+    if (k_new && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
         return PKV_EINVAL;
     const int n = balanced_groups(Hkv, D, block_size, kv_dtype);
     if (n <= 0)
@@ -355,6 +396,8 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     const Fmt fmt = format_of(kv_dtype, Hkv);
     a.sc_blk = fmt.sc_blk;
     a.sc_head = fmt.sc_head;
+    a.k_new = k_new;
+    a.v_new = v_new;
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv);
     ws.ngroups_launched = n;
@@ -368,6 +411,40 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     const bool nt = stream_kv_loads(num_blocks, block_size, Hkv, D, kv_dtype);
     return launched(pkv::launch_decode_balanced(a, ws, D, block_size, fmt.kvf, nt,
                                                 (hipStream_t)stream));
+}
+
+int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
+                                    const void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_tables,
+                                    int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                    int32_t num_blocks, int32_t kv_dtype, float scale,
+                                    void* workspace, int64_t workspace_bytes, float* out,
+                                    float* lse_out, void* stream)
+{
+    return balanced_call(query, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                         block_tables, max_blocks, context_lens, B, Hq, Hkv, D, block_size,
+                         num_blocks, kv_dtype, scale, workspace, workspace_bytes, out, lse_out,
+                         stream);
+}
+
+int paged_append_decode_attention_balanced(const uint16_t* query, const uint16_t* k_new,
+                                           const uint16_t* v_new, void* k_cache,
+                                           void* v_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* block_tables,
+                                           int32_t max_blocks, const int32_t* context_lens,
+                                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                           int32_t block_size, int32_t num_blocks,
+                                           int32_t kv_dtype, float scale, void* workspace,
+                                           int64_t workspace_bytes, float* out, float* lse_out,
+                                           void* stream)
+{
+    if (B > 0 && (!k_new || !v_new))
+        return PKV_EINVAL;
+    return balanced_call(query, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                         block_tables, max_blocks, context_lens, B, Hq, Hkv, D, block_size,
+                         num_blocks, kv_dtype, scale, workspace, workspace_bytes, out, lse_out,
+                         stream);
 }
 
 int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows, const int32_t* query_start,
@@ -658,7 +735,7 @@ int split_context_reduce(const float* partial_out, const float* partial_lse,
 {
     if (B < 0 || Hq <= 0 || D <= 0 || split_tokens <= 0 || max_splits <= 0)
         return PKV_EINVAL;
-    if (max_splits > kMaxSplits || D % 4 != 0 || D > 1024)
+    if (D % 4 != 0 || D > 1024)
         return PKV_EUNSUPPORTED;
     if (B == 0)
         return PKV_OK;

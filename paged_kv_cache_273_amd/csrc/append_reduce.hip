@@ -20,73 +20,6 @@ namespace {
 // One thread moves 8 elements (16 bytes of bf16 input) of one (b, h) row.
 // fp8 ([B] "FP8 KV cache"): code = E4M3FN(float(x) / scale) with a
 // correctly rounded binary32 division; int8: see f32_to_u8_zp.
-// INT8 ([B] "INT8 KV cache"): code = clamp(rint(x / scale) + zero point,
-// 0, 255) with a correctly rounded binary32 division and round-half-even;
-// NaN gives 0.
-__device__ __forceinline__ uint32_t f32_to_u8_zp(float x, float scale, float zp)
-{
-    const float y = x / scale;
-    if (y != y)
-        return 0u;
-    const float v = __builtin_rintf(y) + zp;
-    return (uint32_t)fminf(fmaxf(v, 0.f), 255.f);
-}
-
-// Scales (and int8 zero points) of one (block, kv head).
-struct Quant {
-    float ks, vs, kz, vz;
-};
-
-template <int KVF>
-__device__ __forceinline__ Quant quant_of(const float* k_scale, const float* v_scale, int p,
-                                          int h, int sc_blk, int sc_head)
-{
-    Quant q = {1.f, 1.f, 0.f, 0.f};
-    if (KVF) {
-        const size_t i = (size_t)p * sc_blk + (size_t)h * sc_head;
-        q.ks = k_scale[i];
-        q.vs = v_scale[i];
-        if (KVF == 2) {
-            q.kz = k_scale[i + 1];
-            q.vz = v_scale[i + 1];
-        }
-    }
-    return q;
-}
-
-// Moves 8 elements (16 bytes of bf16 input) of one K row and one V row
-// into the cache at element offset dst, encoding for 1-byte formats.
-template <int KVF>
-__device__ __forceinline__ void store8(const uint16_t* k_src, const uint16_t* v_src,
-                                       void* k_cache, void* v_cache, size_t dst, Quant q)
-{
-    const u32x4 kx = *(const u32x4*)k_src;
-    const u32x4 vx = *(const u32x4*)v_src;
-    if (!KVF) {
-        *(u32x4*)((uint16_t*)k_cache + dst) = kx;
-        *(u32x4*)((uint16_t*)v_cache + dst) = vx;
-        return;
-    }
-    u32x2 kq = {0u, 0u}, vq = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float kf = bf16_bits_to_f32((kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
-        const float vf = bf16_bits_to_f32((vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
-        uint32_t kc, vc;
-        if (KVF == 1) {
-            kc = f32_to_e4m3_sat(kf / q.ks);
-            vc = f32_to_e4m3_sat(vf / q.vs);
-        } else {
-            kc = f32_to_u8_zp(kf, q.ks, q.kz);
-            vc = f32_to_u8_zp(vf, q.vs, q.vz);
-        }
-        kq[i / 4] |= kc << (8 * (i & 3));
-        vq[i / 4] |= vc << (8 * (i & 3));
-    }
-    *(u32x2*)((uint8_t*)k_cache + dst) = kq;
-    *(u32x2*)((uint8_t*)v_cache + dst) = vq;
-}
-
 template <int KVF>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 {
@@ -140,32 +73,22 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a)
 }
 
 // ---------------------------------------------------------------- reduce
-// One 256-thread work-group per (b, hq).  Threads first take the live
-// splits' lse values (M = max, w_s = exp(lse_s - M), W = sum w_s) and park
-// w_s in LDS; then thread (group g, column c) sums w_s * o_s over the
-// splits s = g, g + NG, ... for four output elements, four splits' loads
-// at a time; the NG partial sums meet in LDS.
+// One 256-thread work-group per (b, hq); thread (group g, column c) owns
+// four output elements and the splits s = g, g + NG, ...  Each thread keeps
+// a running log-sum-exp state over its own splits (max m, weight sum w,
+// weighted sum of outputs), kBatch splits' lse values and outputs loaded
+// at a time with no dependence between them, so a row of up to
+// kBatch * NG splits costs one round trip to memory; the NG group states
+// then meet in LDS (the log-sum-exp merge is exact whatever the grouping
+// of the splits).
 constexpr int kReduceThreads = 256;
-
-__device__ __forceinline__ float block_reduce(float v, float* scratch, bool is_max)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = is_max ? wave_max(v) : wave_sum(v);
-    __syncthreads();
-    if (lane == 0)
-        scratch[wave] = v;
-    __syncthreads();
-    float r = scratch[0];
-    for (int i = 1; i < kReduceThreads / kWave; ++i)
-        r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
-    return r;
-}
+constexpr int kReduceBatch = 8;
 
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a)
 {
-    extern __shared__ f32x4 red[];               // [kReduceThreads] then weights
-    float* w_lds = (float*)(red + kReduceThreads);
-    float* scratch = (float*)red;
+    __shared__ f32x4 acc_lds[kReduceThreads];
+    __shared__ float m_lds[kReduceThreads];
+    __shared__ float w_lds[kReduceThreads];
     const int row = blockIdx.x;                  // b * Hq + hq
     const int b = row / a.Hq;
     const int tid = threadIdx.x;
@@ -174,62 +97,74 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a)
     const float* pl = a.partial_lse + (size_t)row * a.max_splits;
     const float* po = a.partial_out + (size_t)row * a.max_splits * a.D;
     float* o = a.out + (size_t)row * a.D;
-
-    float m = -__builtin_inff();
-    for (int s = tid; s < ns; s += kReduceThreads)
-        m = fmaxf(m, pl[s]);
-    m = block_reduce(m, scratch, true);
-    if (m == -__builtin_inff()) {
-        for (int d = tid; d < a.D; d += kReduceThreads)
-            o[d] = 0.f;
-        if (a.lse_out && tid == 0)
-            a.lse_out[row] = -__builtin_inff();
-        return;
-    }
-    float wsum = 0.f;
-    for (int s = tid; s < ns; s += kReduceThreads) {
-        const float l = pl[s];
-        const float w = (l == -__builtin_inff()) ? 0.f : __expf(l - m);
-        w_lds[s] = w;
-        wsum += w;
-    }
-    wsum = block_reduce(wsum, scratch, false);   // also orders the w_lds writes
-    const int cols = a.D / 4;
-    const int ng = kReduceThreads / cols;
+    const int cols = a.D / 4;                    // D % 4 == 0, D <= 1024
+    const int ng = kReduceThreads / cols;        // >= 1; threads past ng * cols idle
     const int col = tid % cols;
     const int grp = tid / cols;
+    constexpr float kNegInf = -__builtin_inff();
+
+    float m = kNegInf, w = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (grp < ng) {
-        // four splits' loads in flight per step
-        constexpr int kBatch = 4;
-        for (int s0 = grp; s0 < ns; s0 += kBatch * ng) {
-            f32x4 v[kBatch];
-            float w[kBatch];
+    for (int s0 = grp < ng ? grp : ns; s0 < ns; s0 += kReduceBatch * ng) {
+        float l[kReduceBatch];
+        f32x4 v[kReduceBatch];
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                const int s = s0 + k * ng;
-                w[k] = s < ns ? w_lds[s] : 0.f;
-                v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (w[k] != 0.f)
-                    v[k] = *(const f32x4*)(po + (size_t)s * a.D + 4 * col);
+        for (int k = 0; k < kReduceBatch; ++k) {
+            const int s = s0 + k * ng;
+            l[k] = kNegInf;
+            v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s < ns) {
+                l[k] = pl[s];
+                v[k] = *(const f32x4*)(po + (size_t)s * a.D + 4 * col);
             }
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                acc += w[k] * v[k];
         }
+        float mb = m;
+#pragma unroll
+        for (int k = 0; k < kReduceBatch; ++k)
+            mb = fmaxf(mb, l[k]);
+        if (mb == kNegInf)
+            continue;                            // nothing visible yet
+        const float c = __expf(m - mb);          // m = -inf: 0
+        acc *= c;
+        w *= c;
+#pragma unroll
+        for (int k = 0; k < kReduceBatch; ++k) {
+            if (l[k] == kNegInf)
+                continue;                        // empty split (or not loaded)
+            const float e = __expf(l[k] - mb);
+            acc += e * v[k];
+            w += e;
+        }
+        m = mb;
     }
+    acc_lds[tid] = acc;
+    m_lds[tid] = m;
+    w_lds[tid] = w;
     __syncthreads();
-    red[tid] = acc;
-    __syncthreads();
-    if (tid < cols) {
-        f32x4 t = red[tid];
-        for (int g = 1; g < ng; ++g)
-            t += red[g * cols + tid];
-        const float inv = 1.0f / wsum;
-        *(f32x4*)(o + 4 * tid) = t * inv;
+    if (tid >= cols)
+        return;
+    float M = kNegInf;
+    for (int g = 0; g < ng; ++g)
+        M = fmaxf(M, m_lds[g * cols + tid]);
+    if (M == kNegInf) {                          // empty sequence or no finite lse
+        *(f32x4*)(o + 4 * tid) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.lse_out && tid == 0)
+            a.lse_out[row] = kNegInf;
+        return;
     }
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    for (int g = 0; g < ng; ++g) {
+        const float mg = m_lds[g * cols + tid];
+        if (mg == kNegInf)
+            continue;
+        const float e = __expf(mg - M);
+        t += e * acc_lds[g * cols + tid];
+        W += e * w_lds[g * cols + tid];
+    }
+    *(f32x4*)(o + 4 * tid) = t * (1.0f / W);
     if (a.lse_out && tid == 0)
-        a.lse_out[row] = m + __logf(wsum);
+        a.lse_out[row] = M + __logf(W);
 }
 
 } // namespace
@@ -276,9 +211,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
         return hipSuccess;
     if (rows > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
-    const size_t lds = kReduceThreads * sizeof(f32x4) + (size_t)a.max_splits * sizeof(float);
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kReduceThreads), lds, stream,
-                       a);
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kReduceThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -187,14 +187,44 @@ __device__ __forceinline__ Cols<1> decode_cols(const DecodeArgs& a, int b, int h
     return cs;
 }
 
+// The step's new K/V row of (b, h) into the cache slot of position t,
+// encoded as paged_kv_append does ([B] "What the KV Cache Stores and Why":
+// only the new token's K and V are computed in a decode step); lanes
+// 0 .. D/8 - 1 move 8 elements each.
+template <int D, int BS, int KVF>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int b, int h, int t)
+{
+    const int lane = __lane_id();
+    if (lane < D / 8) {
+        const int p = a.block_tables[(size_t)b * a.max_blocks + t / BS];
+        const size_t src = ((size_t)b * a.Hkv + h) * D + 8 * lane;
+        const size_t dst = (((size_t)p * BS + t % BS) * a.Hkv + h) * D + 8 * lane;
+        store8<KVF>(a.k_new + src, a.v_new + src, (void*)a.k_cache, (void*)a.v_cache, dst,
+                    quant_of<KVF>(a.k_scale, a.v_scale, p, h, a.sc_blk, a.sc_head));
+    }
+}
+
+// Orders this wave's cache stores before its later loads of the same
+// slots (other lanes read what a lane wrote).
+__device__ __forceinline__ void stores_before_loads()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // One wave attends its columns (kv head h of sequence b) over the logical
 // tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.  With
 // CAUSAL, tokens at or past a column's limit are masked as well; a column
-// that sees no token of the range ends with l = 0.
+// that sees no token of the range ends with l = 0.  append_last: first
+// write the step's new row of (b, h) into slot t_end - 1 (the sequence's
+// last position), ordered before the loads of the last tile; the wait
+// for the stores is placed where the wave waits for its current K tile
+// anyway.
 template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
                                              int h, int t_begin, int t_end,
-                                             const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT])
+                                             const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT],
+                                             bool append_last = false)
 {
     using C = Cfg<D, KVF>;
     constexpr bool FOLD = KVF == 2 && NCT == 1;   // int8 zero points outside the MFMA
@@ -202,6 +232,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     const int q4 = lane >> 4;
     const int r16 = lane & 15;
     const int Hkv = a.Hkv;
+    if (append_last)
+        append_row<D, BS, KVF>(a, b, h, t_end - 1);
 
     // Q^T operands: column r16 of tile j is this lane's query (zero if
     // dead); in registers for one column tile, in LDS for several.
@@ -499,12 +531,16 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         n_plain = max(0, min(n_plain, (min(t_end, cs.mask_from) - t_begin) / kTile));
     Tile<D, KVF> tl;
     TileAddr ta = tile_addr(t_begin);
+    if (append_last && ntiles == 1)
+        stores_before_loads();
     load_k(ta, tl);
     load_v(ta, tl);
     auto step = [&](int it, bool masked) {
         const int t0 = t_begin + kTile * it;
         const TileAddr tn = tile_addr(t0 + kTile);
         stage_v(t0, ta, tl, false);
+        if (append_last && it == ntiles - 2)
+            stores_before_loads();             // tile tn holds slot t_end - 1
         load_v(tn, tl);
         f32x4 sacc[NCT][2];
         qk(ta, tl, sacc);
@@ -549,14 +585,21 @@ __device__ __forceinline__ void finish_range(const RangeAcc<D>& r, float& inv, f
     lse = (r.m + __builtin_log2f(l)) * kLn2;
 }
 
-// Writes this lane's normalised output values of its head column.
-template <int D>
+// Writes this lane's normalised output values of its head column.  NTS:
+// non-temporal stores, for partials another launch reads (they then leave
+// no dirty lines for the end-of-kernel write-back of the L2s).
+template <int D, bool NTS = false>
 __device__ __forceinline__ void store_row(float* o, const RangeAcc<D>& r, float inv)
 {
     const int q4 = __lane_id() >> 4;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-        *(f32x4*)(o + 16 * dt + 4 * q4) = r.acc[dt] * inv;
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const f32x4 v = r.acc[dt] * inv;
+        if (NTS)
+            __builtin_nontemporal_store(v, (f32x4*)(o + 16 * dt + 4 * q4));
+        else
+            *(f32x4*)(o + 16 * dt + 4 * q4) = v;
+    }
 }
 
 template <int D>
@@ -611,16 +654,17 @@ void decode_kernel(DecodeArgs a)
     }
     RangeAcc<D> r[1];
     attend_range<D, BS, KVF, NT, 1, false>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin,
-                                           t_end, decode_cols(a, b, h, D), r);
+                                           t_end, decode_cols(a, b, h, D), r,
+                                           a.k_new != nullptr && t_end == T);
     float inv, lse;
     finish_range<D>(r[0], inv, lse);
     if (!live_col)
         return;
     if (SPLIT) {
         const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
-        store_row<D>(a.partial_out + row * D, r[0], inv);
+        store_row<D, true>(a.partial_out + row * D, r[0], inv);
         if (q4 == 0)
-            a.partial_lse[row] = lse;
+            __builtin_nontemporal_store(lse, a.partial_lse + row);
     } else {
         store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r[0], inv);
         if (a.lse_out && q4 == 0)
@@ -743,7 +787,6 @@ template <int D, int BS, int KVF, int NT, int NCT, bool MQ>
 __global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 {
-    using C = Cfg<D, KVF>;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_all[];  // HG slices
 
     const int q4 = __lane_id() >> 4;
@@ -790,7 +833,8 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         if (!MQ) {
             RangeAcc<D> acc[1];
             attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
-                                                   decode_cols(a, b, h, D), acc);
+                                                   decode_cols(a, b, h, D), acc,
+                                                   a.k_new != nullptr && pend == uend);
             float inv, lse;
             finish_range<D>(acc[0], inv, lse);
             if (r16 < G) {

@@ -199,4 +199,71 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float y)
     return sign | (uint32_t)m;                  // 0..8 (8 == smallest normal)
 }
 
+// INT8 ([B] "INT8 KV cache"): code = clamp(rint(x / scale) + zero point,
+// 0, 255) with a correctly rounded binary32 division and round-half-even;
+// NaN gives 0.
+__device__ __forceinline__ uint32_t f32_to_u8_zp(float x, float scale, float zp)
+{
+    const float y = x / scale;
+    if (y != y)
+        return 0u;
+    const float v = __builtin_rintf(y) + zp;
+    return (uint32_t)fminf(fmaxf(v, 0.f), 255.f);
+}
+
+// Scales (and int8 zero points) of one (block, kv head).
+struct Quant {
+    float ks, vs, kz, vz;
+};
+
+template <int KVF>
+__device__ __forceinline__ Quant quant_of(const float* k_scale, const float* v_scale, int p,
+                                          int h, int sc_blk, int sc_head)
+{
+    Quant q = {1.f, 1.f, 0.f, 0.f};
+    if (KVF) {
+        const size_t i = (size_t)p * sc_blk + (size_t)h * sc_head;
+        q.ks = k_scale[i];
+        q.vs = v_scale[i];
+        if (KVF == 2) {
+            q.kz = k_scale[i + 1];
+            q.vz = v_scale[i + 1];
+        }
+    }
+    return q;
+}
+
+// Moves 8 elements (16 bytes of bf16 input) of one K row and one V row
+// into the cache at element offset dst, encoding for 1-byte formats.
+template <int KVF>
+__device__ __forceinline__ void store8(const uint16_t* k_src, const uint16_t* v_src,
+                                       void* k_cache, void* v_cache, size_t dst, Quant q)
+{
+    const u32x4 kx = *(const u32x4*)k_src;
+    const u32x4 vx = *(const u32x4*)v_src;
+    if (!KVF) {
+        *(u32x4*)((uint16_t*)k_cache + dst) = kx;
+        *(u32x4*)((uint16_t*)v_cache + dst) = vx;
+        return;
+    }
+    u32x2 kq = {0u, 0u}, vq = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float kf = bf16_bits_to_f32((kx[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        const float vf = bf16_bits_to_f32((vx[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        uint32_t kc, vc;
+        if (KVF == 1) {
+            kc = f32_to_e4m3_sat(kf / q.ks);
+            vc = f32_to_e4m3_sat(vf / q.vs);
+        } else {
+            kc = f32_to_u8_zp(kf, q.ks, q.kz);
+            vc = f32_to_u8_zp(vf, q.vs, q.vz);
+        }
+        kq[i / 4] |= kc << (8 * (i & 3));
+        vq[i / 4] |= vc << (8 * (i & 3));
+    }
+    *(u32x2*)((uint8_t*)k_cache + dst) = kq;
+    *(u32x2*)((uint8_t*)v_cache + dst) = vq;
+}
+
 } // namespace pkv

@@ -37,6 +37,12 @@ struct DecodeArgs {
     int32_t sc_blk, sc_head;     // scale of (block p, head h): k_scale[p * sc_blk + h * sc_head]
     int32_t total_rows;   // several new tokens: rows of query / out
     float scale_log2;     // softmax scale * log2(e)
+    // Append fused into the decode launch: the step's new K/V rows
+    // [B, Hkv, D] bf16, written (encoded like paged_kv_append) into slot
+    // T_b - 1 of the caches above by the wave that attends that slot, before
+    // it loads it; null: the caches are only read.
+    const uint16_t* k_new = nullptr;
+    const uint16_t* v_new = nullptr;
 };
 
 // The unit a work-group starts but leaves unfinished (b < 0: none), with

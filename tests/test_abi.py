@@ -39,7 +39,9 @@ def test_header_declares_the_boundary():
                             "paged_decode_workspace_size", "paged_kv_write",
                             "paged_multiquery_attention", "paged_multiquery_workspace_size",
                             "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
-                            "paged_kv_copy_blocks", "pkv_status_string"]), names
+                            "paged_kv_copy_blocks", "pkv_status_string",
+                            "paged_append_decode_attention",
+                            "paged_append_decode_attention_balanced"]), names
 
 
 def test_block_manager_header_declares_its_calls():
@@ -113,10 +115,32 @@ def test_reduce_rejects(pkv):
     f = 0x1000
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 0, 4, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 32, 0, f, None, None) == -1
-    assert L.split_context_reduce(f, f, f, 1, 8, 64, 32, 20000, f, None, None) == -2
+    assert L.split_context_reduce(f, f, f, 1, 8, 2048, 32, 4, f, None, None) == -2
     assert L.split_context_reduce(f, f, f, 1, 8, 66, 32, 4, f, None, None) == -2
     assert L.split_context_reduce(f, f, None, 1, 8, 64, 32, 4, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 0, 8, 64, 32, 4, f, None, None) == 0
+
+
+def _fused(pkv, name, kn, vn, B=1, **kw):
+    f = 0x1000  # never dereferenced: every call below fails its host checks
+    if name == "paged_append_decode_attention":
+        return pkv.lib().paged_append_decode_attention(
+            f, kn, vn, f, f, None, None, f, 4, f, B, 8, 2, 64, 16, 8, 0, 0.125, 0, f, None,
+            None, 0, None, None)
+    return pkv.lib().paged_append_decode_attention_balanced(
+        f, kn, vn, f, f, None, None, f, 4, f, B, 8, 2, 64, 16, 8, 0, 0.125, f, 1 << 20, f,
+        None, None)
+
+
+@pytest.mark.parametrize("name", ["paged_append_decode_attention",
+                                  "paged_append_decode_attention_balanced"])
+def test_fused_append_rejects(pkv, name):
+    f = 0x1000
+    assert _fused(pkv, name, None, f) == -1          # no k_new
+    assert _fused(pkv, name, f, None) == -1          # no v_new
+    assert _fused(pkv, name, 0x1008, f) == -1        # misaligned k_new
+    assert _fused(pkv, name, f, 0x1004) == -1        # misaligned v_new
+    assert _fused(pkv, name, f, f, B=0) == 0         # empty batch: nothing to do
 
 
 def _balanced(pkv, **kw):
