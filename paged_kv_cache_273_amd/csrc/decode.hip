@@ -68,6 +68,10 @@ constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 #define PKV_MIN_WAVES_PER_EU 2
 #endif
 constexpr int kTile = 32;
+// SIMDs of an MI355X (256 CUs x 4): the split decode gives each wave two
+// consecutive splits when that still leaves one wave per SIMD (measured:
+// 1024 longer streams beat 2048 shorter ones by ~1% at 512-token splits)
+constexpr long long kSimds = 256LL * 4;
 
 // K/V loads, with or without the non-temporal hint.  A cache much larger
 // than the 256 MB MALL is read once per call and should stream (NT = 1):
@@ -612,12 +616,17 @@ __device__ __forceinline__ void store_empty_row(float* o)
 }
 
 // Fixed partition: one wave per (b, h) over the whole context, or per
-// (b, h, split) over [s * split_tokens, min(T, (s + 1) * split_tokens)).
-template <int D, int BS, int KVF, int NT, bool SPLIT>
+// (b, h, group of SPW consecutive splits); split s covers
+// [s * split_tokens, min(T, (s + 1) * split_tokens)) and leaves its own
+// partial.  Fewer, longer streams keep HBM closer to its peak (a plain
+// streaming read: 7.0 TB/s from 1024 waves, 6.2-6.5 TB/s from 4096 or
+// more).
+template <int D, int BS, int KVF, int NT, bool SPLIT, int SPW>
 __global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_kernel(DecodeArgs a)
 {
     using C = Cfg<D, KVF>;
+    static_assert(SPW == 1 || SPLIT, "split groups only on the split partition");
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
 
     const int q4 = __lane_id() >> 4;
@@ -626,25 +635,19 @@ void decode_kernel(DecodeArgs a)
     const int unit = blockIdx.x * kWavesPerGroup + wave;
     const int h = unit % a.Hkv;
     int rest = unit / a.Hkv;
-    int split = 0;
+    int split0 = 0;
     if (SPLIT) {
-        split = rest % a.max_splits;
-        rest /= a.max_splits;
+        const int groups = (a.max_splits + SPW - 1) / SPW;
+        split0 = (rest % groups) * SPW;
+        rest /= groups;
     }
     const int b = rest;
     if (b >= a.B)
         return;
     const int T = a.context_lens[b];
-    int t_begin = 0, t_end = T;
-    if (SPLIT) {
-        t_begin = split * a.split_tokens;
-        if (t_begin >= T)
-            return;
-        t_end = min(T, t_begin + a.split_tokens);
-    }
     const int hq = h * a.G + r16;
     const bool live_col = r16 < a.G;
-    if (t_end <= t_begin) {                  // empty sequence, single pass
+    if (!SPLIT && T <= 0) {                   // empty sequence, single pass
         if (live_col) {
             store_empty_row<D>(a.out + ((size_t)b * a.Hq + hq) * D);
             if (a.lse_out && q4 == 0)
@@ -652,23 +655,35 @@ void decode_kernel(DecodeArgs a)
         }
         return;
     }
-    RangeAcc<D> r[1];
-    attend_range<D, BS, KVF, NT, 1, false>(a, lds_all + wave * C::LDS_BYTES, b, h, t_begin,
-                                           t_end, decode_cols(a, b, h, D), r,
-                                           a.k_new != nullptr && t_end == T);
-    float inv, lse;
-    finish_range<D>(r[0], inv, lse);
-    if (!live_col)
-        return;
-    if (SPLIT) {
-        const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
-        store_row<D, true>(a.partial_out + row * D, r[0], inv);
-        if (q4 == 0)
-            __builtin_nontemporal_store(lse, a.partial_lse + row);
-    } else {
-        store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r[0], inv);
-        if (a.lse_out && q4 == 0)
-            a.lse_out[(size_t)b * a.Hq + hq] = lse;
+    unsigned char* lds = lds_all + wave * C::LDS_BYTES;
+#pragma unroll 1
+    for (int k = 0; k < SPW; ++k) {
+        const int split = split0 + k;
+        int t_begin = 0, t_end = T;
+        if (SPLIT) {
+            t_begin = split * a.split_tokens;
+            if (split >= a.max_splits || t_begin >= T)
+                return;
+            t_end = min(T, t_begin + a.split_tokens);
+        }
+        RangeAcc<D> r[1];
+        attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
+                                               decode_cols(a, b, h, D), r,
+                                               a.k_new != nullptr && t_end == T);
+        float inv, lse;
+        finish_range<D>(r[0], inv, lse);
+        if (!live_col)
+            continue;
+        if (SPLIT) {
+            const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
+            store_row<D, true>(a.partial_out + row * D, r[0], inv);
+            if (q4 == 0)
+                __builtin_nontemporal_store(lse, a.partial_lse + row);
+        } else {
+            store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r[0], inv);
+            if (a.lse_out && q4 == 0)
+                a.lse_out[(size_t)b * a.Hq + hq] = lse;
+        }
     }
 }
 
@@ -1100,17 +1115,22 @@ template <int D, int BS, int KVF, int NT>
 hipError_t launch_fixed_t(const DecodeArgs& a, hipStream_t stream)
 {
     const bool split = a.split_tokens > 0;
-    const long long units = (long long)a.B * a.Hkv * (split ? a.max_splits : 1);
+    const long long splits = (long long)a.B * a.Hkv * (split ? a.max_splits : 1);
+    // two consecutive splits per wave while that still leaves a wave per SIMD
+    const int spw = (split && splits >= 2 * kSimds) ? 2 : 1;
+    const long long units = (long long)a.B * a.Hkv * (split ? (a.max_splits + spw - 1) / spw : 1);
     const long long groups = (units + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups <= 0)
         return hipSuccess;
     if (groups > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)groups), block(kWavesPerGroup * kWave);
-    if (split)
-        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true>), grid, block, 0, stream, a);
+    if (split && spw == 2)
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true, 2>), grid, block, 0, stream, a);
+    else if (split)
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true, 1>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, false, 1>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -215,6 +215,33 @@ def test_mqa_mha(orc, pkv, Hkv, Hq):
     assert_close(out, ref, f"Hkv={Hkv} Hq={Hq}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("split", [64, 96])
+def test_split_pairs_per_wave(orc, pkv, kv, split):
+    """Batches with at least 2048 (sequence, kv head, split) units give each
+    wave two consecutive splits; ragged contexts leave odd split counts,
+    a missing second split and splits that end mid-tile."""
+    ctx = tuple(EDGE_CTX[i % len(EDGE_CTX)] + 7 * (i // len(EDGE_CTX)) for i in range(64))
+    wl = make_workload(TINY, B=64, Hq=64, Hkv=8, D=128, block_size=16, ctx_fixed=ctx,
+                       max_blocks=(max(ctx) + 15) // 16 + 1, pool="holes10", kv_dtype=kv,
+                       seed=4100 + split)
+    inp = generate(wl)
+    assert wl.B * wl.Hkv * pkv.max_splits_for(max(ctx), split) >= 2048
+    print(f"split pairs kv={kv} split={split}", flush=True)
+    if kv == "fp8":
+        kc, vc, ks, vs = fp8_group(orc, inp)
+        d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
+        kp, vp = host_appended(orc, inp, kv_dtype="fp8", k_pool=kc, v_pool=vc, ks=ks, vs=vs)
+        ref, rlse = _oracle(orc, inp, kp, vp, kv_dtype="fp8", ks=ks, vs=vs)
+    else:
+        d = DeviceInputs(inp)
+        kp, vp = host_appended(orc, inp)
+        ref, rlse = _oracle(orc, inp, kp, vp)
+    out, lse = run_step(pkv, d, split_tokens=split, want_lse=True)
+    assert_close(out, ref, "split pairs")
+    assert_close(lse, rlse, "split pairs lse")
+
+
 def test_reduce_alone(orc, pkv):
     """split_context_reduce on random partials (with empty splits)."""
     from synthetic import random_partials
