@@ -201,3 +201,44 @@ def test_fused_rejects_missing_rows(pkv):
     d = Dev(inp, inp.k_pool[0], inp.v_pool[0], None, None, "bf16")
     with pytest.raises(Exception):
         pkv.paged_append_decode_attention(d.q, d.k_new, None, d.k, d.v, d.bt, d.cl, 0.125)
+
+
+@pytest.mark.parametrize("mode,split", [("single", 0), ("split", 32), ("split", 512),
+                                        ("balanced", 0)])
+def test_empty_and_one_token_sequences(orc, pkv, mode, split):
+    """T = 0 sequences are neither written nor attended (out 0, lse -inf);
+    T = 1 sequences attend only the row the call itself writes (= V)."""
+    ctx = (0, 5000, 0, 1, 33, 7000, 0, 64, 1)
+    wl = make_workload("llama70b_b64_ragged1k_16k_bs32", B=len(ctx), ctx_fixed=ctx,
+                       max_blocks=220, Hq=16, Hkv=2, seed=5100)
+    inp = generate(wl)
+    what = f"fused empty {mode} {split}"
+    print(what, flush=True)
+    d = Dev(inp, inp.k_pool[0], inp.v_pool[0], None, None, "bf16")
+    out, lse = _fused(pkv, inp, d, mode, split)
+    kp, vp, ref, rlse = _oracle_step(orc, inp, inp.k_pool[0], inp.v_pool[0], None, None, "bf16")
+    assert np.array_equal(d.k.cpu().numpy().view(kp.dtype), kp), what
+    assert np.array_equal(d.v.cpu().numpy().view(vp.dtype), vp), what
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for b in (0, 2, 6):
+        assert np.all(o[b] == 0) and np.all(np.isneginf(l[b])), b
+    keep = [1, 3, 4, 5, 7, 8]
+    assert_close(o[keep], ref[keep], what)
+    assert_close(l[keep], rlse[keep], what + " lse")
+    # one token: out is exactly that token's V row (softmax weight 1)
+    from synthetic import f32_from_bf16_bits
+    for b in (3, 8):
+        v = f32_from_bf16_bits(inp.v_new[0][b]).astype(np.float32)     # [Hkv, D]
+        assert np.array_equal(o[b], np.repeat(v, wl.G, axis=0)), b
+
+
+def test_fused_deterministic(pkv):
+    """Two fused calls on the same inputs give the same bits (the second call
+    rewrites the same rows)."""
+    inp = generate(make_workload("llama70b_b64_ragged1k_16k_bs32", B=16,
+                                 ctx_uniform=(100, 3000), max_blocks=100, Hq=16, Hkv=2))
+    d = Dev(inp, inp.k_pool[0], inp.v_pool[0], None, None, "bf16")
+    outs = [_fused(pkv, inp, d, mode, 64)[0].clone() for mode in ("balanced", "balanced")]
+    assert torch.equal(outs[0], outs[1])
+    outs = [_fused(pkv, inp, d, "split", 64)[0].clone() for _ in range(2)]
+    assert torch.equal(outs[0], outs[1])
