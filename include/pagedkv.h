@@ -215,10 +215,12 @@ int split_context_reduce(const float* partial_out, const float* partial_lse,
  * sequences of every length share one decode iteration) a fixed
  * one-unit-per-(sequence, head) grid leaves most compute units idle
  * while the longest sequences finish.  Here the 32-token tiles of all
- * (sequence, kv head) pairs form one list that is cut into as many equal
- * ranges as the GPU runs waves at once; a pair cut by range boundaries is
- * finished by a log-sum-exp merge of its pieces (second launch, same
- * stream).
+ * (sequence, kv head) pairs form one list that is cut into equal ranges,
+ * one per launched work-group (a group of kv heads walks a range
+ * together; every group starts at once: one group per compute unit for
+ * four-head groups of bf16 / fp8 caches, as many as fit otherwise); a
+ * pair cut by range boundaries is finished by a log-sum-exp merge of its
+ * pieces (second launch, same stream).
  *
  *  workspace       : device scratch of at least workspace_bytes, 16-byte
  *                    aligned, owned by the caller; its contents on entry are

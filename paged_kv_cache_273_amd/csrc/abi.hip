@@ -265,7 +265,7 @@ static int resident_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t k
     if (hipGetDevice(&dev) != hipSuccess)
         return 0;
     const int kvf = format_of(kv_dtype, Hkv).kvf;
-    const int hg = pkv::balanced_head_group(Hkv);
+    const int hg = pkv::balanced_head_group(Hkv, nct, kvf);
     const uint64_t key = ((((((uint64_t)dev * 256 + D) * 64 + block_size) * 4 + kvf) * 16 + hg)
                           * 4 + nct);
     static std::mutex mu;
@@ -279,8 +279,10 @@ static int resident_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t k
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    const int per_cu = nct == 0 ? pkv::balanced_groups_per_cu(D, block_size, kvf, hg)
-                                : pkv::multiquery_groups_per_cu(D, block_size, kvf, hg, nct);
+    int per_cu = nct == 0 ? pkv::balanced_groups_per_cu(D, block_size, kvf, hg)
+                          : pkv::multiquery_groups_per_cu(D, block_size, kvf, hg, nct);
+    if (pkv::balanced_one_group_per_cu(Hkv, nct, kvf) && per_cu > 1)
+        per_cu = 1;
     const int n = cus * per_cu;
     if (n > 0) {
         std::lock_guard<std::mutex> g(mu);
@@ -313,9 +315,9 @@ static void carve_workspace(pkv::BalanceArgs& ws, void* workspace, int64_t rows_
     ws.cuts = (pkv::CutRecord*)((char*)workspace + (parts + 15) / 16 * 16);
 }
 
-static int64_t balanced_bytes(int ngroups, int32_t Hkv, int32_t G, int32_t D)
+static int64_t balanced_bytes(int ngroups, int32_t Hkv, int32_t G, int32_t D, int kvf)
 {
-    return schedule_bytes(ngroups, (int64_t)pkv::balanced_head_group(Hkv) * G, D);
+    return schedule_bytes(ngroups, (int64_t)pkv::balanced_head_group(Hkv, 0, kvf) * G, D);
 }
 
 int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
@@ -330,7 +332,7 @@ int64_t paged_decode_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t 
     const int n = balanced_groups(Hkv, D, block_size, kv_dtype);
     if (n <= 0)
         return PKV_ELAUNCH;
-    return balanced_bytes(n, Hkv, Hq / Hkv, D);
+    return balanced_bytes(n, Hkv, Hq / Hkv, D, format_of(kv_dtype, Hkv).kvf);
 }
 
 // Decode attention on the balanced schedule; with k_new / v_new the launch
@@ -369,7 +371,7 @@ static int balanced_call(const uint16_t* query, const uint16_t* k_new, const uin
     if (n <= 0)
         return PKV_ELAUNCH;
     const int32_t G = Hq / Hkv;
-    if (workspace_bytes < balanced_bytes(n, Hkv, G, D))
+    if (workspace_bytes < balanced_bytes(n, Hkv, G, D, format_of(kv_dtype, Hkv).kvf))
         return PKV_EINVAL;
     pkv::DecodeArgs a;
     a.query = query;
@@ -399,7 +401,7 @@ static int balanced_call(const uint16_t* query, const uint16_t* k_new, const uin
     a.k_new = k_new;
     a.v_new = v_new;
     pkv::BalanceArgs ws;
-    ws.head_group = pkv::balanced_head_group(Hkv);
+    ws.head_group = pkv::balanced_head_group(Hkv, 0, fmt.kvf);
     ws.ngroups_launched = n;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * G, D);
     // range boundaries are computed in double precision: keep
@@ -513,9 +515,9 @@ static int mq_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t kv_dtyp
     return resident_groups(Hkv, D, block_size, kv_dtype, nct);
 }
 
-static int64_t mq_bytes(int ngroups, int32_t Hkv, int nct, int32_t D)
+static int64_t mq_bytes(int ngroups, int32_t Hkv, int nct, int32_t D, int kvf)
 {
-    return schedule_bytes(ngroups, (int64_t)pkv::balanced_head_group(Hkv) * 16 * nct, D);
+    return schedule_bytes(ngroups, (int64_t)pkv::balanced_head_group(Hkv, nct, kvf) * 16 * nct, D);
 }
 
 int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
@@ -532,7 +534,7 @@ int64_t paged_multiquery_workspace_size(int32_t Hq, int32_t Hkv, int32_t D, int3
     const int n = mq_groups(Hkv, D, block_size, kv_dtype, nct);
     if (n <= 0)
         return PKV_ELAUNCH;
-    return mq_bytes(n, Hkv, nct, D);
+    return mq_bytes(n, Hkv, nct, D, format_of(kv_dtype, Hkv).kvf);
 }
 
 int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start,
@@ -573,7 +575,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     const int n = mq_groups(Hkv, D, block_size, kv_dtype, nct);
     if (n <= 0)
         return PKV_ELAUNCH;
-    if (workspace_bytes < mq_bytes(n, Hkv, nct, D))
+    if (workspace_bytes < mq_bytes(n, Hkv, nct, D, format_of(kv_dtype, Hkv).kvf))
         return PKV_EINVAL;
     pkv::DecodeArgs a;
     a.query = query;
@@ -601,7 +603,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     a.sc_blk = fmt.sc_blk;
     a.sc_head = fmt.sc_head;
     pkv::BalanceArgs ws;
-    ws.head_group = pkv::balanced_head_group(Hkv);
+    ws.head_group = pkv::balanced_head_group(Hkv, nct, fmt.kvf);
     ws.ngroups_launched = n;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * 16 * nct, D);
     // range boundaries in double precision: (tiles of the call) * (groups

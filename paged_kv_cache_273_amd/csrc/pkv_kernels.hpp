@@ -133,8 +133,12 @@ hipError_t launch_prefill(const DecodeArgs& a, int max_query_len, int D, int blo
                           int kvf, bool nt, hipStream_t stream);
 // resident work-groups per compute unit of the multi-query kernel (0 on error)
 int multiquery_groups_per_cu(int D, int block_size, int kv_dtype, int head_group, int nct);
-// kv heads per work-group of the balanced decode for Hkv kv heads
-int balanced_head_group(int Hkv);
+// kv heads per work-group of the balanced schedule for Hkv kv heads
+// (nct = 0: decode; 1 or 2: the multi-query kernel's column tiles; kvf:
+// kernel format 0/1/2)
+int balanced_head_group(int Hkv, int nct, int kvf);
+// whether that schedule launches one work-group per CU (else as many as fit)
+bool balanced_one_group_per_cu(int Hkv, int nct, int kvf);
 // resident work-groups per compute unit of the balanced decode (0 on error)
 int balanced_groups_per_cu(int D, int block_size, int kv_dtype, int head_group);
 

@@ -295,15 +295,17 @@ def test_balanced_tiny(orc, pkv, scale):
 @pytest.mark.parametrize("G", [1, 8, 16])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("D", [64, 128])
-def test_balanced_shapes(orc, pkv, D, bs, G, kv):
+@pytest.mark.parametrize("Hkv", [2, 4, 8])
+def test_balanced_shapes(orc, pkv, D, bs, G, kv, Hkv):
     """Few tiles against thousands of waves: nearly every unit is cut into
-    one-tile pieces on different waves, so the merge carries the result."""
-    Hkv = 2
+    one-tile pieces on different waves, so the merge carries the result.
+    Hkv 4 and 8 run four-head work-groups (two head groups per sequence at
+    Hkv 8), Hkv 2 two-head groups."""
     wl = make_workload(TINY, B=len(EDGE_CTX), Hq=G * Hkv, Hkv=Hkv, D=D, block_size=bs,
                        ctx_fixed=EDGE_CTX, max_blocks=(300 + bs - 1) // bs + 1,
                        pool="holes10", kv_dtype=kv, seed=2000 + D + bs + G)
     inp = generate(wl)
-    print(f"balanced shape D={D} bs={bs} G={G} kv={kv}", flush=True)
+    print(f"balanced shape D={D} bs={bs} G={G} kv={kv} Hkv={Hkv}", flush=True)
     if kv == "fp8":
         kc, vc, ks, vs = fp8_group(orc, inp)
         d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
@@ -318,10 +320,11 @@ def test_balanced_shapes(orc, pkv, D, bs, G, kv):
     assert_close(lse, rlse, "balanced lse")
 
 
-def test_balanced_empty_and_ragged(orc, pkv):
+@pytest.mark.parametrize("Hkv", [2, 8])
+def test_balanced_empty_and_ragged(orc, pkv, Hkv):
     ctx = (0, 5000, 0, 1, 33, 7000, 0, 64)
     wl = make_workload("llama70b_b64_ragged1k_16k_bs32", B=len(ctx), ctx_fixed=ctx,
-                       max_blocks=220, Hq=16, Hkv=2)
+                       max_blocks=220, Hq=8 * Hkv, Hkv=Hkv)
     inp = generate(wl)
     d = DeviceInputs(inp)
     out, lse = run_balanced(pkv, d)
