@@ -216,6 +216,14 @@ __device__ __forceinline__ void stores_before_loads()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Segment hook of attend_range: nothing to emit.
+struct NoSegments {
+    template <int D, int NCT>
+    __device__ void operator()(int, RangeAcc<D> (&)[NCT]) const
+    {
+    }
+};
+
 // One wave attends its columns (kv head h of sequence b) over the logical
 // tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.  With
 // CAUSAL, tokens at or past a column's limit are masked as well; a column
@@ -223,12 +231,17 @@ __device__ __forceinline__ void stores_before_loads()
 // write the step's new row of (b, h) into slot t_end - 1 (the sequence's
 // last position), ordered before the loads of the last tile; the wait
 // for the stores is placed where the wave waits for its current K tile
-// anyway.
-template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL>
+// anyway.  seg_tiles > 0: the range is a run of segments of seg_tiles
+// tiles (consecutive context splits); at each segment end but the last,
+// emit(segment, r) takes the segment's finished state and r restarts,
+// while the next segment's first tile is already streaming in.  The last
+// segment's state is left in r as for a single range.
+template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL, typename Emit = NoSegments>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
                                              int h, int t_begin, int t_end,
                                              const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT],
-                                             bool append_last = false)
+                                             bool append_last = false, int seg_tiles = 0,
+                                             Emit emit = Emit())
 {
     using C = Cfg<D, KVF>;
     constexpr bool FOLD = KVF == 2 && NCT == 1;   // int8 zero points outside the MFMA
@@ -366,15 +379,32 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         }
     };
 
+    auto reset = [&]() {
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
+        for (int j = 0; j < NCT; ++j) {
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-            r[j].acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        r[j].m = -__builtin_inff();
-        r[j].l = 0.f;
-        r[j].corr = 0.f;
-    }
+            for (int dt = 0; dt < C::DT; ++dt)
+                r[j].acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            r[j].m = -__builtin_inff();
+            r[j].l = 0.f;
+            r[j].corr = 0.f;
+        }
+    };
+    // int8 zero points: subtract each column's accumulated correction
+    auto apply_fold = [&]() {
+        if (FOLD) {
+#pragma unroll
+            for (int j = 0; j < NCT; ++j) {
+                float c = r[j].corr;
+                c += xor_shuffle(c, 16);
+                c += xor_shuffle(c, 32);
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+                    r[j].acc[dt] -= c;
+            }
+        }
+    };
+    reset();
     const float sl2 = a.scale_log2;
 
     // V rows -> LDS as bf16 (zeroed past the range end).
@@ -551,6 +581,11 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         load_k(tn, tl);
         softmax_pv(t0, ta, sacc, masked);
         ta = tn;
+        if (seg_tiles > 0 && (it + 1) % seg_tiles == 0) {   // a segment ends here
+            apply_fold();
+            emit(it / seg_tiles, r);
+            reset();
+        }
     };
     for (int it = 0; it < n_plain; ++it)
         step(it, false);
@@ -564,17 +599,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         qk(ta, tl, sacc);
         softmax_pv(t0, ta, sacc, true);
     }
-    if (FOLD) {
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-            float c = r[j].corr;
-            c += xor_shuffle(c, 16);
-            c += xor_shuffle(c, 32);
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-                r[j].acc[dt] -= c;
-        }
-    }
+    apply_fold();
 }
 
 // Sums the per-lane normalisers of each head column; returns 1/l and the
@@ -656,35 +681,42 @@ void decode_kernel(DecodeArgs a)
         return;
     }
     unsigned char* lds = lds_all + wave * C::LDS_BYTES;
-#pragma unroll 1
-    for (int k = 0; k < SPW; ++k) {
-        const int split = split0 + k;
-        int t_begin = 0, t_end = T;
-        if (SPLIT) {
-            t_begin = split * a.split_tokens;
-            if (split >= a.max_splits || t_begin >= T)
-                return;
-            t_end = min(T, t_begin + a.split_tokens);
-        }
+    // the partial of split s (normalised output and natural-log lse)
+    auto store_split = [&](int split, RangeAcc<D> (&rr)[1]) {
+        float inv, lse;
+        finish_range<D>(rr[0], inv, lse);
+        if (!live_col)
+            return;
+        const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
+        store_row<D, true>(a.partial_out + row * D, rr[0], inv);
+        if (q4 == 0)
+            __builtin_nontemporal_store(lse, a.partial_lse + row);
+    };
+    if (!SPLIT) {
         RangeAcc<D> r[1];
-        attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
-                                               decode_cols(a, b, h, D), r,
-                                               a.k_new != nullptr && t_end == T);
+        attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, 0, T, decode_cols(a, b, h, D), r,
+                                               a.k_new != nullptr);
         float inv, lse;
         finish_range<D>(r[0], inv, lse);
         if (!live_col)
-            continue;
-        if (SPLIT) {
-            const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
-            store_row<D, true>(a.partial_out + row * D, r[0], inv);
-            if (q4 == 0)
-                __builtin_nontemporal_store(lse, a.partial_lse + row);
-        } else {
-            store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r[0], inv);
-            if (a.lse_out && q4 == 0)
-                a.lse_out[(size_t)b * a.Hq + hq] = lse;
-        }
+            return;
+        store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, r[0], inv);
+        if (a.lse_out && q4 == 0)
+            a.lse_out[(size_t)b * a.Hq + hq] = lse;
+        return;
     }
+    // SPW consecutive splits in one pass: the stream does not stop at a
+    // split boundary (split_tokens is a multiple of the tile when SPW > 1)
+    const int t_begin = split0 * a.split_tokens;
+    if (split0 >= a.max_splits || t_begin >= T)
+        return;
+    const int t_end = (int)min((long long)T, (long long)t_begin + (long long)SPW * a.split_tokens);
+    RangeAcc<D> r[1];
+    auto emit = [&](int seg, RangeAcc<D> (&rr)[1]) { store_split(split0 + seg, rr); };
+    attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end, decode_cols(a, b, h, D),
+                                           r, a.k_new != nullptr && t_end == T,
+                                           SPW > 1 ? a.split_tokens / kTile : 0, emit);
+    store_split(split0 + (t_end - 1 - t_begin) / a.split_tokens, r);
 }
 
 // ---------------------------------------------------------------- balanced
@@ -1117,7 +1149,8 @@ hipError_t launch_fixed_t(const DecodeArgs& a, hipStream_t stream)
     const bool split = a.split_tokens > 0;
     const long long splits = (long long)a.B * a.Hkv * (split ? a.max_splits : 1);
     // two consecutive splits per wave while that still leaves a wave per SIMD
-    const int spw = (split && splits >= 2 * kSimds) ? 2 : 1;
+    const int spw =
+        (split && splits >= 2 * kSimds && a.split_tokens % kTile == 0) ? 2 : 1;
     const long long units = (long long)a.B * a.Hkv * (split ? (a.max_splits + spw - 1) / spw : 1);
     const long long groups = (units + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups <= 0)

@@ -62,25 +62,27 @@ class DeviceInputs:
 
 
 def run_step(pkv, d: DeviceInputs, layer=0, split_tokens=0, scale=None, append=True,
-             want_lse=False):
-    """append (optional) + attention (+ reduce when split).  Returns out, lse."""
+             want_lse=False, kv_dtype=None):
+    """append (optional) + attention (+ reduce when split).  Returns out, lse.
+    kv_dtype: the cache format name (default: inferred from the cache dtype)."""
     inp = d.inp
     wl = inp.wl
     sc = float(inp.scale) if scale is None else float(scale)
+    fmt = None if kv_dtype in (None, "bf16", "fp8") else kv_dtype
     if append:
         pkv.paged_kv_append(d.k_new, d.v_new, d.k, d.v, d.bt, d.cl, k_scale=d.ks,
-                            v_scale=d.vs)
+                            v_scale=d.vs, kv_dtype=fmt)
     lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device=dev()) if want_lse else None
     if split_tokens == 0:
         out = pkv.paged_decode_attention(d.q[layer], d.k, d.v, d.bt, d.cl, sc, lse_out=lse,
-                                         k_scale=d.ks, v_scale=d.vs)
+                                         k_scale=d.ks, v_scale=d.vs, kv_dtype=fmt)
     else:
         ms = pkv.max_splits_for(int(inp.context_lens.max()), split_tokens)
         po = torch.full((wl.B, wl.Hq, ms, wl.D), float("nan"), device=dev())
         pl = torch.full((wl.B, wl.Hq, ms), float("nan"), device=dev())
         pkv.paged_decode_attention(d.q[layer], d.k, d.v, d.bt, d.cl, sc,
                                    split_tokens=split_tokens, partial_out=po, partial_lse=pl,
-                                   k_scale=d.ks, v_scale=d.vs)
+                                   k_scale=d.ks, v_scale=d.vs, kv_dtype=fmt)
         out = pkv.split_context_reduce(po, pl, d.cl, split_tokens, lse_out=lse)
     torch.cuda.synchronize()
     return out, lse

@@ -215,12 +215,15 @@ def test_mqa_mha(orc, pkv, Hkv, Hq):
     assert_close(out, ref, f"Hkv={Hkv} Hq={Hq}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("split", [64, 96])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("split", [64, 96, 80])
 def test_split_pairs_per_wave(orc, pkv, kv, split):
     """Batches with at least 2048 (sequence, kv head, split) units give each
-    wave two consecutive splits; ragged contexts leave odd split counts,
-    a missing second split and splits that end mid-tile."""
+    wave two consecutive splits in one pass (the split boundary emits a
+    partial while the next tile streams in; int8 applies its zero-point
+    correction per split); ragged contexts leave odd split counts, a
+    missing second split and splits that end mid-tile.  80 is not a
+    multiple of the 32-token tile: one split per wave."""
     ctx = tuple(EDGE_CTX[i % len(EDGE_CTX)] + 7 * (i // len(EDGE_CTX)) for i in range(64))
     wl = make_workload(TINY, B=64, Hq=64, Hkv=8, D=128, block_size=16, ctx_fixed=ctx,
                        max_blocks=(max(ctx) + 15) // 16 + 1, pool="holes10", kv_dtype=kv,
@@ -233,11 +236,20 @@ def test_split_pairs_per_wave(orc, pkv, kv, split):
         d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
         kp, vp = host_appended(orc, inp, kv_dtype="fp8", k_pool=kc, v_pool=vc, ks=ks, vs=vs)
         ref, rlse = _oracle(orc, inp, kp, vp, kv_dtype="fp8", ks=ks, vs=vs)
+    elif kv == "int8":
+        sc = [orc.int8_block_params(src, inp.block_tables, inp.context_lens, wl.block_size,
+                                    symmetric=False) for src in (inp.k_pool[0], inp.v_pool[0])]
+        kc = orc.quantize_pool(inp.k_pool[0], sc[0], "int8")
+        vc = orc.quantize_pool(inp.v_pool[0], sc[1], "int8")
+        d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=sc[0], v_scale=sc[1])
+        kp, vp = host_appended(orc, inp, kv_dtype="int8", k_pool=kc, v_pool=vc, ks=sc[0],
+                               vs=sc[1])
+        ref, rlse = _oracle(orc, inp, kp, vp, kv_dtype="int8", ks=sc[0], vs=sc[1])
     else:
         d = DeviceInputs(inp)
         kp, vp = host_appended(orc, inp)
         ref, rlse = _oracle(orc, inp, kp, vp)
-    out, lse = run_step(pkv, d, split_tokens=split, want_lse=True)
+    out, lse = run_step(pkv, d, split_tokens=split, want_lse=True, kv_dtype=kv)
     assert_close(out, ref, "split pairs")
     assert_close(lse, rlse, "split pairs lse")
 
