@@ -819,6 +819,15 @@ __device__ __forceinline__ long long range_start(long long r, long long total, l
     return (long long)__builtin_floor((double)(r * total) / (double)R);
 }
 
+// Work-groups that get a range: every launched one, or one per tile when
+// the call has fewer tiles than work-groups, so that no range is empty and
+// the merge walks one work-group per piece (a sequence of a few tiles
+// spread over hundreds of empty ranges cost the merge ~39 us).
+__device__ __forceinline__ long long ranges_of(long long launched, long long total)
+{
+    return total < 1 ? 1 : (total < launched ? total : launched);
+}
+
 // The work-group whose range holds linear tile x.
 __device__ __forceinline__ long long range_of(long long x, long long total, long long R)
 {
@@ -840,17 +849,17 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const int r16 = __lane_id() & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head within group
     const long long r = blockIdx.x;
-    const long long R = ws.ngroups_launched;
     const int HG = ws.head_group;
     const int ngroups = a.Hkv / HG;
     const int G = a.G;
     constexpr int kCols = 16 * NCT;                  // MQ columns per wave
     const int cpw = MQ ? kCols : G;                  // workspace rows per wave
     const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
+    const long long R = ranges_of(ws.ngroups_launched, total);
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
     CutRecord cut = {0, total, 0, -1, 0, 0, 0, 0, 0};
-    if (r0 >= r1) {
+    if (r >= R || r0 >= r1) {
         if (threadIdx.x == 0)
             ws.cuts[r] = cut;
         return;
@@ -984,12 +993,11 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     constexpr int npg = kWave / cols;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long R = ws.ngroups_launched;
     const int HG = ws.head_group;
     const int G = a.G;
     constexpr int kCols = 16 * NCT;
     const int cpw = MQ ? kCols : G;
-    if ((long long)blockIdx.x == R) {
+    if ((long long)blockIdx.x == ws.ngroups_launched) {
         if (MQ)
             return;
         for (int b = blockIdx.y; b < a.B; b += gridDim.y) {
@@ -1031,6 +1039,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     }
     float* o = a.out + orow * D;
     const long long total = rec.total;
+    const long long R = ranges_of(ws.ngroups_launched, total);
     const long long ustart = rec.ustart;
     const long long rf = blockIdx.x;
     const long long rl = rec.rl;
