@@ -70,7 +70,7 @@ constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 constexpr int kTile = 32;
 // SIMDs of an MI355X (256 CUs x 4): the split decode gives each wave two
 // consecutive splits when that still leaves one wave per SIMD (measured:
-// 1024 longer streams beat 2048 shorter ones by ~1% at 512-token splits)
+// 1024 longer streams beat 2048 shorter ones by ~2% at 512-token splits)
 constexpr long long kSimds = 256LL * 4;
 
 // K/V loads, with or without the non-temporal hint.  A cache much larger
@@ -644,8 +644,8 @@ __device__ __forceinline__ void store_empty_row(float* o)
 // (b, h, group of SPW consecutive splits); split s covers
 // [s * split_tokens, min(T, (s + 1) * split_tokens)) and leaves its own
 // partial.  Fewer, longer streams keep HBM closer to its peak (a plain
-// streaming read: 7.0 TB/s from 1024 waves, 6.2-6.5 TB/s from 4096 or
-// more).
+// streaming read: 7.0 TB/s from 1024 waves with 8 KB in flight each,
+// 6.0-6.8 TB/s from 2048-16384 waves).
 template <int D, int BS, int KVF, int NT, bool SPLIT, int SPW>
 __global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_kernel(DecodeArgs a)
