@@ -402,7 +402,11 @@ static int balanced_call(const uint16_t* query, const uint16_t* k_new, const uin
     a.v_new = v_new;
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv, 0, fmt.kvf);
-    ws.ngroups_launched = n;
+    // with four-head groups, the Hkv / 4 groups covering one token range
+    // run side by side (neighbouring work-groups), so each 2 KB token row is
+    // read whole at one time (measured ~1% faster than a range per group)
+    ws.head_split = pkv::balanced_one_group_per_cu(Hkv, 0, fmt.kvf) ? Hkv / ws.head_group : 1;
+    ws.ngroups_launched = n / ws.head_split * ws.head_split;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * G, D);
     // range boundaries are computed in double precision: keep
     // (tiles of the call) * (groups launched) below 2^52
@@ -604,6 +608,7 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     a.sc_head = fmt.sc_head;
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv, nct, fmt.kvf);
+    ws.head_split = 1;
     ws.ngroups_launched = n;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * 16 * nct, D);
     // range boundaries in double precision: (tiles of the call) * (groups

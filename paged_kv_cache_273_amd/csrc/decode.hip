@@ -848,20 +848,26 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const int q4 = __lane_id() >> 4;
     const int r16 = __lane_id() & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head within group
-    const long long r = blockIdx.x;
+    // NS work-groups share each range, work-group hs of them taking kv
+    // heads [(u * NS + hs) * HG, +HG) of list unit u: the halves of a token
+    // row are then read at the same time by neighbouring work-groups
+    const int NS = ws.head_split;
+    const long long wg = blockIdx.x;
+    const int hs = (int)(wg % NS);
+    const long long r = wg / NS;                     // range
     const int HG = ws.head_group;
-    const int ngroups = a.Hkv / HG;
+    const int ngroups = a.Hkv / (HG * NS);           // list units per sequence (x col groups)
     const int G = a.G;
     constexpr int kCols = 16 * NCT;                  // MQ columns per wave
     const int cpw = MQ ? kCols : G;                  // workspace rows per wave
     const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
-    const long long R = ranges_of(ws.ngroups_launched, total);
+    const long long R = ranges_of(ws.ngroups_launched / NS, total);
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
     CutRecord cut = {0, total, 0, -1, 0, 0, 0, 0, 0};
     if (r >= R || r0 >= r1) {
         if (threadIdx.x == 0)
-            ws.cuts[r] = cut;
+            ws.cuts[wg] = cut;
         return;
     }
     int b;
@@ -881,11 +887,12 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         const long long pend = uend < r1 ? uend : r1;
         const int t_begin = (int)(x - ustart) * kTile;
         const int t_end = min(T, (int)(pend - ustart) * kTile);
-        const int hg = MQ ? u / ncg : u;
-        const int cg = MQ ? u - hg * ncg : 0;
+        const int hl = MQ ? u / ncg : u;             // head group within the list
+        const int cg = MQ ? u - hl * ncg : 0;
+        const int hg = hl * NS + hs;
         const int h = hg * HG + wave;
         const bool whole = x == ustart && pend == uend;
-        const size_t slot = 2 * (size_t)r + (piece == 0 ? 0 : 1);
+        const size_t slot = 2 * (size_t)wg + (piece == 0 ? 0 : 1);
         if (!MQ) {
             RangeAcc<D> acc[1];
             attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
@@ -972,7 +979,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         }
     }
     if (threadIdx.x == 0)
-        ws.cuts[r] = cut;
+        ws.cuts[wg] = cut;
 }
 
 // Merge of the recorded cut units.  Work-group (r, y) takes the unit that
@@ -1020,10 +1027,12 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     const int in_slot = blockIdx.y * kMergeWaves + wave;   // w * cpw + column
     if (in_slot >= HG * cpw)
         return;
+    const int NS = ws.head_split;
+    const int hs = (int)(blockIdx.x % NS);           // record of work-group blockIdx.x
     const int u = rec.u;
-    const int hg = MQ ? u / rec.ncg : u;
-    const int cg = MQ ? u - hg * rec.ncg : 0;
-    const int h = hg * HG + in_slot / cpw;
+    const int hl = MQ ? u / rec.ncg : u;
+    const int cg = MQ ? u - hl * rec.ncg : 0;
+    const int h = (hl * NS + hs) * HG + in_slot / cpw;
     const int cc = in_slot % cpw;
     size_t orow;
     if (!MQ) {
@@ -1039,9 +1048,9 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     }
     float* o = a.out + orow * D;
     const long long total = rec.total;
-    const long long R = ranges_of(ws.ngroups_launched, total);
+    const long long R = ranges_of(ws.ngroups_launched / NS, total);
     const long long ustart = rec.ustart;
-    const long long rf = blockIdx.x;
+    const long long rf = blockIdx.x / NS;             // range holding the first piece
     const long long rl = rec.rl;
     const int rows_per_slot = HG * cpw;
     // Groups between rf and rl with an empty range (fewer tiles than
@@ -1050,7 +1059,7 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
         const long long s0 = range_start(r, total, R);
         if (range_start(r + 1, total, R) <= s0)
             return -1;
-        const long long slot = 2 * r + ((r == rf && s0 < ustart) ? 1 : 0);
+        const long long slot = 2 * (r * NS + hs) + ((r == rf && s0 < ustart) ? 1 : 0);
         return slot * rows_per_slot + in_slot;
     };
     const int p0 = lane / cols;

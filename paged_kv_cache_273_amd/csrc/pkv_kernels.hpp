@@ -50,8 +50,9 @@ struct DecodeArgs {
 struct CutRecord {
     long long ustart;         // linear index of the unit's first tile
     long long total;          // tiles of the whole call
-    long long rl;             // work-group holding the unit's last tile
-    int32_t b, u;             // sequence, unit of the sequence (head group, column group)
+    long long rl;             // range holding the unit's last tile
+    int32_t b, u;             // sequence, unit of the sequence in the tile list (head
+                              // group of the list, column group)
     int32_t n, ncg;           // tiles of the unit, column groups of the sequence
     int32_t qs, q;            // several new tokens: first row and rows of the sequence
 };
@@ -64,8 +65,10 @@ struct BalanceArgs {
     float* part_out;          // [2 * ngroups_launched, head_group * C, D]
     float* part_lse;          // [2 * ngroups_launched, head_group * C]
     CutRecord* cuts;          // [ngroups_launched], 16-byte aligned
-    int32_t ngroups_launched; // work-groups (token ranges) of the decode launch
+    int32_t ngroups_launched; // work-groups of the decode launch (a multiple of head_split)
     int32_t head_group;       // kv heads per work-group (divides Hkv, <= 8)
+    int32_t head_split;       // work-groups sharing each token range (their head groups
+                              // together cover head_group * head_split kv heads)
 };
 
 // Several new K/V rows per sequence: rows query_start[b] .. query_start[b+1]-1
