@@ -287,3 +287,17 @@ def test_block_moves_reject(pkv):
     c = L.paged_kv_copy_blocks
     assert c(f, f, None, None, f, None, 2, 16, 2, 64, 8, 0, None) == -1
     assert c(f, f, None, None, f, f, 0, 16, 2, 64, 8, 0, None) == 0
+
+
+def test_build_step_does_not_need_the_library():
+    """build() must work on a checkout with no library yet: it reaches the
+    compile step without importing the package (whose import refuses to run
+    before the library exists)."""
+    import subprocess
+    import sys
+
+    code = ("import sys, __graft_entry__ as g; m = g._load_build_module(); "
+            "assert callable(m.build); "
+            "assert 'paged_kv_cache_273_amd' not in sys.modules, 'package imported'")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
