@@ -614,21 +614,17 @@ __device__ __forceinline__ void finish_range(const RangeAcc<D>& r, float& inv, f
     lse = (r.m + __builtin_log2f(l)) * kLn2;
 }
 
-// Writes this lane's normalised output values of its head column.  NTS:
-// non-temporal stores, for partials another launch reads (they then leave
-// no dirty lines for the end-of-kernel write-back of the L2s).
-template <int D, bool NTS = false>
+// Writes this lane's normalised output values of its head column.  Plain
+// stores also for partials that the next launch reads: they stay in the
+// caches for it (split partials written non-temporally made the 32k-token
+// step ~1.7% slower).
+template <int D>
 __device__ __forceinline__ void store_row(float* o, const RangeAcc<D>& r, float inv)
 {
     const int q4 = __lane_id() >> 4;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 v = r.acc[dt] * inv;
-        if (NTS)
-            __builtin_nontemporal_store(v, (f32x4*)(o + 16 * dt + 4 * q4));
-        else
-            *(f32x4*)(o + 16 * dt + 4 * q4) = v;
-    }
+    for (int dt = 0; dt < D / 16; ++dt)
+        *(f32x4*)(o + 16 * dt + 4 * q4) = r.acc[dt] * inv;
 }
 
 template <int D>
@@ -688,9 +684,9 @@ void decode_kernel(DecodeArgs a)
         if (!live_col)
             return;
         const size_t row = ((size_t)b * a.Hq + hq) * a.max_splits + split;
-        store_row<D, true>(a.partial_out + row * D, rr[0], inv);
+        store_row<D>(a.partial_out + row * D, rr[0], inv);
         if (q4 == 0)
-            __builtin_nontemporal_store(lse, a.partial_lse + row);
+            a.partial_lse[row] = lse;
     };
     if (!SPLIT) {
         RangeAcc<D> r[1];
