@@ -64,6 +64,9 @@ def _args():
     p.add_argument("--unfused", action="store_true",
                    help="append with paged_kv_append in its own launch instead of inside "
                         "the attention launch of each cache group's first layer")
+    p.add_argument("--cold-steps", type=int, default=20,
+                   help="extra event-timed steps, each after a 1 GiB write that evicts the "
+                        "MALL and the L2s (cold_cache in the JSON line; 0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -266,6 +269,7 @@ def main():
     step_s = wall / a.steps
     gbs = ideal / step_s / 1e9
     kern_gbs = per_layer / kern_s / 1e9
+    cold = _cold_steps(step, a.cold_steps, ideal, dev) if a.cold_steps > 0 else None
     # algorithmic flops of one attention call: q.k and p.v, 2 per multiply-add,
     # per (row or sequence, query head, visible token, head-dim element)
     if multi:
@@ -337,9 +341,48 @@ def main():
             "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": per_layer,
         }),
         "attention_tflops": round(kern_tflops, 2),
+        "cold_cache": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def _cold_steps(step, n, ideal, dev):
+    """Whole steps timed one by one with a HIP event pair, each after a
+    1 GiB write on the same stream that evicts the 256 MB MALL and the L2s
+    (no K/V byte of the previous step is left in a cache).  The same
+    event-timed measurement of back-to-back steps without the write is
+    reported beside it: the event pair's own marker packets are in both."""
+    import torch
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(evict):
+        pairs = []
+        for i in range(n):
+            if evict:
+                flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(None)
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+        return us[len(us) // 2], us[len(us) // 10], us[min(len(us) - 1, (9 * len(us)) // 10)]
+
+    cold_med, cold_p10, cold_p90 = timed(True)
+    warm_med, _, _ = timed(False)
+    del flush
+    return {
+        "flush_bytes": 1 << 30, "steps": n,
+        "step_us_median": round(cold_med, 2), "step_us_p10": round(cold_p10, 2),
+        "step_us_p90": round(cold_p90, 2),
+        "gbs_median": round(ideal / (cold_med * 1e-6) / 1e9, 1),
+        "frac_median": round(ideal / (cold_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "warm_step_us_median_same_timing": round(warm_med, 2),
+    }
 
 
 HOST_LINK_GBS = 64.0     # PCIe 5.0 x16, one direction
