@@ -80,7 +80,7 @@ def _args():
 def main():
     a = _args()
     if a.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {a.gpus}); "
               "the decode kernel has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
