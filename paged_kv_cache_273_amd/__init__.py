@@ -138,8 +138,65 @@ def _kv_dtype(cache: torch.Tensor, kv_dtype=None) -> int:
 
 
 def _need(t: torch.Tensor, dtypes, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+# Shape checks.  The C ABI receives one B, Hq, Hkv, D, block size and split
+# count per call and cannot see the tensors, so a tensor whose shape
+# disagrees with them would be read or written out of bounds on the device.
+# Every tensor is checked here, before any pointer is taken.
+def _shape(t, shape, name, dtypes=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtypes is not None:
+        _need(t, dtypes, name)
+    elif not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dim() != len(shape) or any(w is not None and int(n) != w
+                                    for n, w in zip(t.shape, shape)):
+        want = tuple("*" if w is None else w for w in shape)
+        raise ValueError(f"{name}: shape {tuple(t.shape)} does not match {want}")
+
+
+def _same_device(ref, **ts):
+    for name, t in ts.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the call's tensors on {ref.device}")
+
+
+def _scale_shape(code, nb, Hkv):
+    return {PKV_FP8_E4M3: (nb, Hkv), PKV_FP8_E4M3_PER_HEAD: (Hkv,),
+            PKV_FP8_E4M3_PER_TENSOR: (1,), PKV_INT8: (nb, Hkv, 2)}.get(code)
+
+
+def _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype):
+    """Checks a K/V cache pair and its scales; returns (num_blocks,
+    block_size, Hkv, D, pkv_dtype code)."""
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be a [num_blocks, block_size, Hkv, D] tensor")
+    nb, bs, Hkv, D = (int(n) for n in k_cache.shape)
+    code = _kv_dtype(k_cache, kv_dtype)
+    _shape(v_cache, (nb, bs, Hkv, D), "v_cache")
+    if v_cache.element_size() != k_cache.element_size():
+        raise TypeError(f"v_cache dtype {v_cache.dtype} differs from k_cache {k_cache.dtype}")
+    sc = _scale_shape(code, nb, Hkv)
+    if sc is not None:
+        _shape(k_scale, sc, "k_scale", (torch.float32,))
+        _shape(v_scale, sc, "v_scale", (torch.float32,))
+    _same_device(k_cache, v_cache=v_cache, k_scale=k_scale if sc else None,
+                 v_scale=v_scale if sc else None)
+    return nb, bs, Hkv, D, code
+
+
+def _table_args(block_tables, context_lens, B):
+    """Checks block_tables [B, max_blocks] and context_lens [B] (int32);
+    returns max_blocks."""
+    _shape(block_tables, (B, None), "block_tables", (torch.int32,))
+    _shape(context_lens, (B,), "context_lens", (torch.int32,))
+    return int(block_tables.shape[1])
 
 
 def _stream(stream):
@@ -152,53 +209,62 @@ def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, 
     """k_new/v_new [B, Hkv, D] bf16; caches [num_blocks, block_size, Hkv, D]
     (bf16 bits or E4M3FN codes); block_tables [B, max_blocks] int32;
     context_lens [B] int32 (including the new token)."""
-    _need(k_new, _BF16_BITS, "k_new")
-    _need(v_new, _BF16_BITS, "v_new")
-    _need(block_tables, (torch.int32,), "block_tables")
-    _need(context_lens, (torch.int32,), "context_lens")
-    B, Hkv, D = k_new.shape
-    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    nb, bs, Hkv, D, code = _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype)
+    _shape(k_new, (None, Hkv, D), "k_new", _BF16_BITS)
+    B = int(k_new.shape[0])
+    _shape(v_new, (B, Hkv, D), "v_new", _BF16_BITS)
+    max_blocks = _table_args(block_tables, context_lens, B)
+    _same_device(k_cache, k_new=k_new, v_new=v_new, block_tables=block_tables,
+                 context_lens=context_lens)
     st = _lib.paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                               _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
-                              block_tables.shape[1], _ptr(context_lens), B, Hkv, D, bs, nb,
-                              _kv_dtype(k_cache, kv_dtype), _stream(stream))
+                              max_blocks, _ptr(context_lens), B, Hkv, D, bs, nb,
+                              code, _stream(stream))
     _check("paged_kv_append", st)
 
 
 def _decode(name, query, new, k_cache, v_cache, block_tables, context_lens, scale, out,
             lse_out, split_tokens, partial_out, partial_lse, k_scale, v_scale, kv_dtype, stream):
-    _need(query, _BF16_BITS, "query")
-    _need(block_tables, (torch.int32,), "block_tables")
-    _need(context_lens, (torch.int32,), "context_lens")
-    B, Hq, D = query.shape
-    nb, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    nb, bs, Hkv, D, code = _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype)
+    _shape(query, (None, None, D), "query", _BF16_BITS)
+    B, Hq = int(query.shape[0]), int(query.shape[1])
+    max_blocks = _table_args(block_tables, context_lens, B)
+    _new_row_args(new, B, Hkv, D)
     max_splits = 0
     if split_tokens == 0:
         if out is None:
             out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
-        _need(out, (torch.float32,), "out")
+        _shape(out, (B, Hq, D), "out", (torch.float32,))
     else:
         if partial_out is None or partial_lse is None:
             raise ValueError("split mode needs partial_out and partial_lse")
-        _need(partial_out, (torch.float32,), "partial_out")
-        _need(partial_lse, (torch.float32,), "partial_lse")
-        max_splits = partial_out.shape[2]
+        _shape(partial_out, (B, Hq, None, D), "partial_out", (torch.float32,))
+        max_splits = int(partial_out.shape[2])
+        _shape(partial_lse, (B, Hq, max_splits), "partial_lse", (torch.float32,))
+    if lse_out is not None:
+        _shape(lse_out, (B, Hq), "lse_out", (torch.float32,))
+    _same_device(k_cache, query=query, block_tables=block_tables, context_lens=context_lens,
+                 out=out, lse_out=lse_out, partial_out=partial_out, partial_lse=partial_lse)
     st = getattr(_lib, name)(
         _ptr(query), *_new_rows(new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-        _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq,
-        Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), float(scale), int(split_tokens),
+        _ptr(v_scale), _ptr(block_tables), max_blocks, _ptr(context_lens), B, Hq,
+        Hkv, D, bs, nb, code, float(scale), int(split_tokens),
         _ptr(out), _ptr(partial_out), _ptr(partial_lse), max_splits, _ptr(lse_out),
         _stream(stream))
     _check(name, st)
     return out if split_tokens == 0 else (partial_out, partial_lse)
 
 
+def _new_row_args(new, B, Hkv, D):
+    if new is not None:
+        _shape(new[0], (B, Hkv, D), "k_new", _BF16_BITS)
+        _shape(new[1], (B, Hkv, D), "v_new", _BF16_BITS)
+
+
 def _new_rows(new):
     if new is None:
         return ()
     k_new, v_new = new
-    _need(k_new, _BF16_BITS, "k_new")
-    _need(v_new, _BF16_BITS, "v_new")
     return (_ptr(k_new), _ptr(v_new))
 
 
@@ -245,19 +311,25 @@ def make_workspace(query, k_cache, kv_dtype=None) -> torch.Tensor:
 
 def _balanced(name, query, new, k_cache, v_cache, block_tables, context_lens, scale, workspace,
               out, lse_out, k_scale, v_scale, kv_dtype, stream):
-    _need(query, _BF16_BITS, "query")
-    _need(block_tables, (torch.int32,), "block_tables")
-    _need(context_lens, (torch.int32,), "context_lens")
-    B, Hq, D = query.shape
-    nb, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    nb, bs, Hkv, D, code = _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype)
+    _shape(query, (None, None, D), "query", _BF16_BITS)
+    B, Hq = int(query.shape[0]), int(query.shape[1])
+    max_blocks = _table_args(block_tables, context_lens, B)
+    _new_row_args(new, B, Hkv, D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
-    _need(out, (torch.float32,), "out")
+    _shape(out, (B, Hq, D), "out", (torch.float32,))
+    if lse_out is not None:
+        _shape(lse_out, (B, Hq), "lse_out", (torch.float32,))
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace: expected a torch.Tensor")
+    _same_device(k_cache, query=query, block_tables=block_tables, context_lens=context_lens,
+                 out=out, lse_out=lse_out, workspace=workspace)
     nbytes = workspace.numel() * workspace.element_size()
     st = getattr(_lib, name)(
         _ptr(query), *_new_rows(new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-        _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq,
-        Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), float(scale), _ptr(workspace), nbytes,
+        _ptr(v_scale), _ptr(block_tables), max_blocks, _ptr(context_lens), B, Hq,
+        Hkv, D, bs, nb, code, float(scale), _ptr(workspace), nbytes,
         _ptr(out), _ptr(lse_out), _stream(stream))
     _check(name, st)
     return out
@@ -288,11 +360,17 @@ def paged_append_decode_attention_balanced(query, k_new, v_new, k_cache, v_cache
 def split_context_reduce(partial_out, partial_lse, context_lens, split_tokens, *, out=None,
                          lse_out=None, stream=None):
     """Merges partials [B, Hq, max_splits, D] into out [B, Hq, D] float32."""
-    _need(partial_out, (torch.float32,), "partial_out")
-    _need(partial_lse, (torch.float32,), "partial_lse")
-    B, Hq, ms, D = partial_out.shape
+    _shape(partial_out, (None, None, None, None), "partial_out", (torch.float32,))
+    B, Hq, ms, D = (int(n) for n in partial_out.shape)
+    _shape(partial_lse, (B, Hq, ms), "partial_lse", (torch.float32,))
+    _shape(context_lens, (B,), "context_lens", (torch.int32,))
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=partial_out.device)
+    _shape(out, (B, Hq, D), "out", (torch.float32,))
+    if lse_out is not None:
+        _shape(lse_out, (B, Hq), "lse_out", (torch.float32,))
+    _same_device(partial_out, partial_lse=partial_lse, context_lens=context_lens, out=out,
+                 lse_out=lse_out)
     st = _lib.split_context_reduce(_ptr(partial_out), _ptr(partial_lse), _ptr(context_lens), B,
                                    Hq, D, int(split_tokens), ms, _ptr(out), _ptr(lse_out),
                                    _stream(stream))
@@ -306,20 +384,19 @@ def paged_kv_write(k_rows, v_rows, query_start, k_cache, v_cache, block_tables, 
     """k_rows/v_rows [rows, Hkv, D] bf16: rows query_start[b] + i go to
     positions context_lens[b] - q_b + i (q_b = query_start[b+1] -
     query_start[b] <= max_query_len)."""
-    _need(k_rows, _BF16_BITS, "k_rows")
-    _need(v_rows, _BF16_BITS, "v_rows")
-    _need(query_start, (torch.int32,), "query_start")
-    _need(block_tables, (torch.int32,), "block_tables")
-    _need(context_lens, (torch.int32,), "context_lens")
-    _, Hkv, D = k_rows.shape
-    B = context_lens.shape[0]
-    if query_start.shape[0] != B + 1:
-        raise ValueError("query_start must hold B + 1 offsets")
-    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    nb, bs, Hkv, D, code = _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype)
+    _shape(k_rows, (None, Hkv, D), "k_rows", _BF16_BITS)
+    _shape(v_rows, tuple(k_rows.shape), "v_rows", _BF16_BITS)
+    _shape(context_lens, (None,), "context_lens", (torch.int32,))
+    B = int(context_lens.shape[0])
+    _shape(query_start, (B + 1,), "query_start (B + 1 offsets)", (torch.int32,))
+    max_blocks = _table_args(block_tables, context_lens, B)
+    _same_device(k_cache, k_rows=k_rows, v_rows=v_rows, query_start=query_start,
+                 block_tables=block_tables, context_lens=context_lens)
     st = _lib.paged_kv_write(_ptr(k_rows), _ptr(v_rows), _ptr(query_start), _ptr(k_cache),
                              _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
-                             block_tables.shape[1], _ptr(context_lens), B, int(max_query_len),
-                             Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), _stream(stream))
+                             max_blocks, _ptr(context_lens), B, int(max_query_len),
+                             Hkv, D, bs, nb, code, _stream(stream))
     _check("paged_kv_write", st)
 
 
@@ -349,23 +426,27 @@ def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_table
     context_lens[b] - q_b + i) attends causally over its sequence's tokens
     up to its own position.  Writes out [rows, Hq, D] float32 (and lse_out
     [rows, Hq]) and returns out."""
-    _need(query, _BF16_BITS, "query")
-    _need(query_start, (torch.int32,), "query_start")
-    _need(block_tables, (torch.int32,), "block_tables")
-    _need(context_lens, (torch.int32,), "context_lens")
-    rows, Hq, D = query.shape
-    B = context_lens.shape[0]
-    if query_start.shape[0] != B + 1:
-        raise ValueError("query_start must hold B + 1 offsets")
-    nb, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    nb, bs, Hkv, D, code = _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype)
+    _shape(query, (None, None, D), "query", _BF16_BITS)
+    rows, Hq = int(query.shape[0]), int(query.shape[1])
+    _shape(context_lens, (None,), "context_lens", (torch.int32,))
+    B = int(context_lens.shape[0])
+    _shape(query_start, (B + 1,), "query_start (B + 1 offsets)", (torch.int32,))
+    max_blocks = _table_args(block_tables, context_lens, B)
     if out is None:
         out = torch.empty((rows, Hq, D), dtype=torch.float32, device=query.device)
-    _need(out, (torch.float32,), "out")
+    _shape(out, (rows, Hq, D), "out", (torch.float32,))
+    if lse_out is not None:
+        _shape(lse_out, (rows, Hq), "lse_out", (torch.float32,))
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace: expected a torch.Tensor")
+    _same_device(k_cache, query=query, query_start=query_start, block_tables=block_tables,
+                 context_lens=context_lens, out=out, lse_out=lse_out, workspace=workspace)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.paged_multiquery_attention(
         _ptr(query), _ptr(query_start), rows, int(max_query_len), _ptr(k_cache), _ptr(v_cache),
-        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), B, Hq, Hkv, D, bs, nb, _kv_dtype(k_cache, kv_dtype), float(scale),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), max_blocks,
+        _ptr(context_lens), B, Hq, Hkv, D, bs, nb, code, float(scale),
         _ptr(workspace), nbytes, _ptr(out), _ptr(lse_out), _stream(stream))
     _check("paged_multiquery_attention", st)
     return out
@@ -386,8 +467,26 @@ def _any_ptr(t):
 
 
 def _move_shape(k_cache, kv_dtype=None):
-    nb, bs, Hkv, D = k_cache.shape
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be a [num_blocks, block_size, Hkv, D] tensor")
+    nb, bs, Hkv, D = (int(n) for n in k_cache.shape)
     return nb, bs, Hkv, D, _kv_dtype(k_cache, kv_dtype)
+
+
+def _block_buffers(k_cache, v_cache, n, bufs, scales, code):
+    """Checks the pool pair and the [n, block_size, Hkv, D] block buffers
+    (and, for formats with per-block scales, [n, Hkv] / [n, Hkv, 2] scale
+    buffers) of a block move."""
+    nb, bs, Hkv, D = (int(x) for x in k_cache.shape)
+    _shape(v_cache, (nb, bs, Hkv, D), "v_cache")
+    for name, t in bufs.items():
+        _shape(t, (n, bs, Hkv, D), name)
+        if t.element_size() != k_cache.element_size():
+            raise TypeError(f"{name}: dtype {t.dtype} differs from the cache's {k_cache.dtype}")
+    per_block = {PKV_FP8_E4M3: (Hkv,), PKV_INT8: (Hkv, 2)}.get(code)
+    for name, (t, rows) in scales.items():
+        if per_block is not None:
+            _shape(t, (rows,) + per_block, name, (torch.float32,))
 
 
 def paged_kv_gather_blocks(k_cache, v_cache, block_ids, k_out, v_out, *, k_scale=None,
@@ -395,8 +494,12 @@ def paged_kv_gather_blocks(k_cache, v_cache, block_ids, k_out, v_out, *, k_scale
                            stream=None):
     """k_out[i] = k_cache[block_ids[i]] (and V, and fp8 scales).  Outputs may
     be pinned host tensors (swap out / offload)."""
-    _need(block_ids, (torch.int32,), "block_ids")
+    _shape(block_ids, (None,), "block_ids", (torch.int32,))
     nb, bs, Hkv, D, dt = _move_shape(k_cache, kv_dtype)
+    n = int(block_ids.shape[0])
+    _block_buffers(k_cache, v_cache, n, {"k_out": k_out, "v_out": v_out},
+                   {"k_scale": (k_scale, nb), "v_scale": (v_scale, nb),
+                    "k_scale_out": (k_scale_out, n), "v_scale_out": (v_scale_out, n)}, dt)
     st = _lib.paged_kv_gather_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _any_ptr(block_ids),
         block_ids.numel(), bs, Hkv, D, nb, dt, _any_ptr(k_out), _any_ptr(v_out),
@@ -409,8 +512,12 @@ def paged_kv_scatter_blocks(k_in, v_in, block_ids, k_cache, v_cache, *, k_scale_
                             stream=None):
     """k_cache[block_ids[i]] = k_in[i] (and V, and fp8 scales).  Inputs may be
     pinned host tensors (swap in)."""
-    _need(block_ids, (torch.int32,), "block_ids")
+    _shape(block_ids, (None,), "block_ids", (torch.int32,))
     nb, bs, Hkv, D, dt = _move_shape(k_cache, kv_dtype)
+    n = int(block_ids.shape[0])
+    _block_buffers(k_cache, v_cache, n, {"k_in": k_in, "v_in": v_in},
+                   {"k_scale": (k_scale, nb), "v_scale": (v_scale, nb),
+                    "k_scale_in": (k_scale_in, n), "v_scale_in": (v_scale_in, n)}, dt)
     st = _lib.paged_kv_scatter_blocks(
         _any_ptr(k_in), _any_ptr(v_in), _any_ptr(k_scale_in), _any_ptr(v_scale_in),
         _any_ptr(block_ids), block_ids.numel(), bs, Hkv, D, nb, dt, _ptr(k_cache), _ptr(v_cache),
@@ -421,11 +528,11 @@ def paged_kv_scatter_blocks(k_in, v_in, block_ids, k_cache, v_cache, *, k_scale_
 def paged_kv_copy_blocks(k_cache, v_cache, src_ids, dst_ids, *, k_scale=None, v_scale=None,
                          kv_dtype=None, stream=None):
     """k_cache[dst_ids[i]] = k_cache[src_ids[i]] (copy-on-write copies)."""
-    _need(src_ids, (torch.int32,), "src_ids")
-    _need(dst_ids, (torch.int32,), "dst_ids")
-    if src_ids.numel() != dst_ids.numel():
-        raise ValueError("src_ids and dst_ids differ in length")
+    _shape(src_ids, (None,), "src_ids", (torch.int32,))
+    _shape(dst_ids, (int(src_ids.shape[0]),), "dst_ids", (torch.int32,))
     nb, bs, Hkv, D, dt = _move_shape(k_cache, kv_dtype)
+    _block_buffers(k_cache, v_cache, 0, {}, {"k_scale": (k_scale, nb), "v_scale": (v_scale, nb)},
+                   dt)
     st = _lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                    _any_ptr(src_ids), _any_ptr(dst_ids), src_ids.numel(), bs, Hkv,
                                    D, nb, dt, _stream(stream))

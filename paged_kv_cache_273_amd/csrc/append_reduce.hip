@@ -93,7 +93,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a)
     const int b = row / a.Hq;
     const int tid = threadIdx.x;
     const int T = a.context_lens[b];
-    const int ns = T > 0 ? (T + a.split_tokens - 1) / a.split_tokens : 0;
+    // splits of the row, never more than its max_splits slots (a context
+    // beyond max_splits * split_tokens breaks the caller's precondition; its
+    // tail was not attended, and no slot outside the row is read)
+    const int ns = T > 0 ? min((T + a.split_tokens - 1) / a.split_tokens, a.max_splits) : 0;
     const float* pl = a.partial_lse + (size_t)row * a.max_splits;
     const float* po = a.partial_out + (size_t)row * a.max_splits * a.D;
     float* o = a.out + (size_t)row * a.D;

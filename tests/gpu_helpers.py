@@ -25,6 +25,17 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a).to(dev())
 
 
+def tables_to_dev(block_tables, context_lens, block_size, num_blocks):
+    """Device copies of a block table and its context lengths, after the
+    oracle's validator has checked the preconditions every kernel relies
+    on (live entries inside the pool, every sequence fits its row)."""
+    import oracle
+
+    st = oracle.check_tables(block_tables, context_lens, block_size, num_blocks)
+    assert st == 0, f"invalid block table: sequence {-st - 1} breaks the preconditions"
+    return to_dev(block_tables), to_dev(context_lens)
+
+
 def bits16(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint16)
 
@@ -55,8 +66,8 @@ class DeviceInputs:
         self.k_new = to_dev(inp.k_new[group])
         self.v_new = to_dev(inp.v_new[group])
         self.q = to_dev(inp.query)
-        self.bt = to_dev(inp.block_tables)
-        self.cl = to_dev(inp.context_lens)
+        self.bt, self.cl = tables_to_dev(inp.block_tables, inp.context_lens,
+                                         inp.wl.block_size, kp.shape[0])
         self.ks = None if k_scale is None else to_dev(k_scale)
         self.vs = None if v_scale is None else to_dev(v_scale)
 

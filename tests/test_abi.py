@@ -8,6 +8,33 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_BUF = []
+
+
+def F():
+    """Address of a real, zeroed, 256-byte aligned 1 MiB buffer that every
+    pointer argument below points into: device memory when a GPU is present,
+    host memory otherwise.  Each call here must fail its host checks; were
+    one to launch anyway, its kernels would find zero context lengths and
+    zero table entries (block 0) inside a valid allocation."""
+    if not _BUF:
+        import numpy as np
+        import torch
+
+        if torch.cuda.is_available():
+            t = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda:0")
+            _BUF.append((t, t.data_ptr()))
+        else:
+            a = np.zeros((1 << 20) + 256, dtype=np.uint8)
+            _BUF.append((a, (a.ctypes.data + 255) // 256 * 256))
+    return _BUF[0][1]
+
+
+def _res(v):
+    """("buf", offset) -> an address inside the real buffer."""
+    return F() + v[1] if isinstance(v, tuple) and v and v[0] == "buf" else v
+
+
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("pagedkv.h", "pkv_block_manager.h")]
 
 
@@ -74,11 +101,10 @@ def _decode(pkv, **kw):
     a = dict(query=None, k=None, v=None, ks=None, vs=None, bt=None, max_blocks=4, cl=None, B=1,
              Hq=8, Hkv=2, D=64, bs=16, nb=8, dt=0, scale=0.125, split=0, out=None, po=None,
              pl=None, ms=0, lse=None)
-    a.update(kw)
-    fake = 0x1000  # never dereferenced: every call below fails its host checks
+    a.update({k: _res(v) for k, v in kw.items()})
     for k in ("query", "k", "v", "bt", "cl", "out"):
         if a[k] is None:
-            a[k] = fake
+            a[k] = F()
     return pkv.lib().paged_decode_attention(
         a["query"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["max_blocks"], a["cl"], a["B"],
         a["Hq"], a["Hkv"], a["D"], a["bs"], a["nb"], a["dt"], a["scale"], a["split"], a["out"],
@@ -98,7 +124,7 @@ def _decode(pkv, **kw):
     ({"split": 32, "ms": 0}, -1),        # split without partial slots
     ({"split": 32, "ms": 4}, -1),        # split without partial buffers
     ({"scale": float("nan")}, -1),
-    ({"query": 0x1002}, -1),             # misaligned query
+    ({"query": ("buf", 2)}, -1),             # misaligned query
     ({"B": -1}, -1),
     ({"nb": 0}, -1),
 ])
@@ -112,7 +138,7 @@ def test_empty_batch_is_a_no_op(pkv):
 
 def test_reduce_rejects(pkv):
     L = pkv.lib()
-    f = 0x1000
+    f = F()
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 0, 4, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 1, 8, 64, 32, 0, f, None, None) == -1
     assert L.split_context_reduce(f, f, f, 1, 8, 2048, 32, 4, f, None, None) == -2
@@ -122,7 +148,7 @@ def test_reduce_rejects(pkv):
 
 
 def _fused(pkv, name, kn, vn, B=1, **kw):
-    f = 0x1000  # never dereferenced: every call below fails its host checks
+    f = F()
     if name == "paged_append_decode_attention":
         return pkv.lib().paged_append_decode_attention(
             f, kn, vn, f, f, None, None, f, 4, f, B, 8, 2, 64, 16, 8, 0, 0.125, 0, f, None,
@@ -135,19 +161,19 @@ def _fused(pkv, name, kn, vn, B=1, **kw):
 @pytest.mark.parametrize("name", ["paged_append_decode_attention",
                                   "paged_append_decode_attention_balanced"])
 def test_fused_append_rejects(pkv, name):
-    f = 0x1000
+    f = F()
     assert _fused(pkv, name, None, f) == -1          # no k_new
     assert _fused(pkv, name, f, None) == -1          # no v_new
-    assert _fused(pkv, name, 0x1008, f) == -1        # misaligned k_new
-    assert _fused(pkv, name, f, 0x1004) == -1        # misaligned v_new
+    assert _fused(pkv, name, f + 8, f) == -1         # misaligned k_new
+    assert _fused(pkv, name, f, f + 4) == -1         # misaligned v_new
     assert _fused(pkv, name, f, f, B=0) == 0         # empty batch: nothing to do
 
 
 def _balanced(pkv, **kw):
-    a = dict(B=1, Hq=8, Hkv=2, D=64, bs=16, nb=8, dt=0, scale=0.125, ws=0x1000, wsb=1 << 20,
-             out=0x1000, max_blocks=4)
-    a.update(kw)
-    f = 0x1000
+    a = dict(B=1, Hq=8, Hkv=2, D=64, bs=16, nb=8, dt=0, scale=0.125, ws=F(), wsb=1 << 20,
+             out=F(), max_blocks=4)
+    a.update({k: _res(v) for k, v in kw.items()})
+    f = F()
     return pkv.lib().paged_decode_attention_balanced(
         f, f, f, None, None, f, a["max_blocks"], f, a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
         a["nb"], a["dt"], a["scale"], a["ws"], a["wsb"], a["out"], None, None)
@@ -162,7 +188,7 @@ def _balanced(pkv, **kw):
     ({"dt": 1}, -1),                     # fp8 without scales
     ({"dt": 4}, -1),                     # int8 without scales
     ({"ws": None}, -1),                  # no workspace
-    ({"ws": 0x1004}, -1),                # misaligned workspace
+    ({"ws": ("buf", 4)}, -1),                # misaligned workspace
     ({"wsb": -5}, -1),
     ({"max_blocks": 1 << 22}, -2),       # more than 2^25 tokens per sequence
     ({"scale": float("inf")}, -1),
@@ -185,18 +211,18 @@ def test_workspace_size_rejects(pkv):
 
 def test_append_rejects(pkv):
     L = pkv.lib()
-    f = 0x1000
+    f = F()
     assert L.paged_kv_append(f, f, f, f, None, None, f, 4, f, 1, 2, 64, 16, 8, 1, None) == -1
     assert L.paged_kv_append(f, f, f, f, None, None, f, 4, f, 1, 2, 80, 16, 8, 0, None) == -2
     assert L.paged_kv_append(f, f, f, f, None, None, f, 4, f, 1, 0, 64, 16, 8, 0, None) == -1
-    assert L.paged_kv_append(0x1008, f, f, f, None, None, f, 4, f, 1, 2, 64, 16, 8, 0,
+    assert L.paged_kv_append(f + 8, f, f, f, None, None, f, 4, f, 1, 2, 64, 16, 8, 0,
                              None) == -1
     assert L.paged_kv_append(f, f, f, f, None, None, f, 4, f, 0, 2, 64, 16, 8, 0, None) == 0
 
 
 def test_write_rejects(pkv):
     L = pkv.lib()
-    f = 0x1000
+    f = F()
     # k_rows, v_rows, qs, k, v, ks, vs, bt, max_blocks, cl, B, max_q, Hkv, D, bs, nb, dt
     ok = [f, f, f, f, f, None, None, f, 4, f, 2, 3, 2, 64, 16, 8, 0, None]
 
@@ -214,7 +240,7 @@ def test_write_rejects(pkv):
     assert call(Hkv=0) == -1
     assert call(mq=-1) == -1
     assert call(qs=None) == -1
-    assert call(kr=0x1008) == -1             # misaligned rows
+    assert call(kr=f + 8) == -1             # misaligned rows
     assert call(B=70000) == -2               # more sequences than one launch column holds
     assert call(B=0) == 0
     assert call(mq=0) == 0
@@ -223,11 +249,11 @@ def test_write_rejects(pkv):
 def _mq(pkv, **kw):
     names = ["q", "qs", "rows", "mq", "k", "v", "ks", "vs", "bt", "mb", "cl", "B", "Hq", "Hkv",
              "D", "bs", "nb", "dt", "scale", "ws", "wsb", "out", "lse", "stream"]
-    f = 0x1000
+    f = F()
     a = [f, f, 12, 4, f, f, None, None, f, 4, f, 3, 8, 2, 64, 16, 8, 0, 0.125, f, 1 << 20, f,
          None, None]
     for k, v in kw.items():
-        a[names.index(k)] = v
+        a[names.index(k)] = _res(v)
     return pkv.lib().paged_multiquery_attention(*a)
 
 
@@ -240,7 +266,7 @@ def _mq(pkv, **kw):
     ({"dt": 1}, -1),                     # fp8 without scales
     ({"dt": 4}, -1),                     # int8 without scales
     ({"ws": None}, -1),
-    ({"ws": 0x1004}, -1),
+    ({"ws": ("buf", 4)}, -1),
     ({"qs": None}, -1),
     ({"mq": 0}, -1),                     # rows but no new tokens
     ({"mq": -2}, -1),
@@ -248,7 +274,7 @@ def _mq(pkv, **kw):
     ({"wsb": -5}, -1),
     ({"mb": 1 << 22}, -2),
     ({"scale": float("nan")}, -1),
-    ({"lse": 0x1002}, -1),               # misaligned lse
+    ({"lse": ("buf", 2)}, -1),               # misaligned lse
 ])
 def test_multiquery_rejects(pkv, kw, status):
     assert _mq(pkv, **kw) == status
@@ -271,14 +297,14 @@ def test_multiquery_workspace_size_rejects(pkv):
 
 def test_block_moves_reject(pkv):
     L = pkv.lib()
-    f = 0x1000
+    f = F()
     g = L.paged_kv_gather_blocks
     # k, v, ks, vs, ids, n, bs, Hkv, D, nb, dt, ko, vo, kso, vso, stream
     assert g(f, f, None, None, f, -1, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
     assert g(f, f, None, None, None, 4, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
     assert g(f, f, None, None, f, 4, 16, 2, 64, 8, 1, f, f, None, None, None) == -1   # fp8, no scales
     assert g(f, f, None, None, f, 4, 1, 1, 7, 8, 1, f, f, f, f, None) == -2          # 7-byte blocks
-    assert g(0x1008, f, None, None, f, 4, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
+    assert g(f + 8, f, None, None, f, 4, 16, 2, 64, 8, 0, f, f, None, None, None) == -1
     assert g(f, f, None, None, f, 0, 16, 2, 64, 8, 0, f, f, None, None, None) == 0
     s = L.paged_kv_scatter_blocks
     assert s(f, f, None, None, f, 4, 16, 2, 64, 0, 0, f, f, None, None, None) == -1  # no blocks

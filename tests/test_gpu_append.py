@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DeviceInputs, bits16, fp8_group, host_appended, to_dev
+from gpu_helpers import DeviceInputs, bits16, fp8_group, host_appended, tables_to_dev, to_dev
 from synthetic import generate, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -92,7 +92,8 @@ def test_fp8_encode_exhaustive(orc, pkv, scales):
         vc = np.zeros((nb, bs, Hkv, D), dtype=np.uint8)
         vbits = bits[::-1].copy()
         dk, dv = to_dev(kc), to_dev(vc)
-        pkv.paged_kv_append(to_dev(bits), to_dev(vbits), dk, dv, to_dev(tables), to_dev(ctx),
+        dbt, dcl = tables_to_dev(tables, ctx, bs, nb)
+        pkv.paged_kv_append(to_dev(bits), to_dev(vbits), dk, dv, dbt, dcl,
                             k_scale=to_dev(ks), v_scale=to_dev(vs))
         torch.cuda.synchronize()
         orc.append(bits, vbits, kc, vc, tables, ctx, bs, kv_dtype="fp8", k_scale=ks,

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from gpu_helpers import (DeviceInputs, assert_close, dev, fp8_group, host_appended, run_step,
-                         sample_rows, to_dev)
+                         sample_rows, tables_to_dev, to_dev)
 from synthetic import bf16_bits_from_f32, f32_from_bf16_bits, generate, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -124,7 +124,7 @@ def test_permutation_is_bit_identical(orc, pkv, split):
     for seed in (1, 2):
         kq, vq, tq = _permuted(inp, kp, vp, seed)
         d2 = DeviceInputs(inp, k_pool=kq, v_pool=vq)
-        d2.bt = to_dev(tq)
+        d2.bt = tables_to_dev(tq, inp.context_lens, inp.wl.block_size, kq.shape[0])[0]
         out, lse = run_step(pkv, d2, split_tokens=split, append=False, want_lse=True)
         assert torch.equal(out, base) and torch.equal(lse, blse)
 
@@ -362,7 +362,7 @@ def test_balanced_deterministic_and_placement_free(orc, pkv):
     assert torch.equal(a, b) and torch.equal(la, lb)
     kq, vq, tq = _permuted(inp, kp, vp, 7)
     d2 = DeviceInputs(inp, k_pool=kq, v_pool=vq)
-    d2.bt = to_dev(tq)
+    d2.bt = tables_to_dev(tq, inp.context_lens, inp.wl.block_size, kq.shape[0])[0]
     c, lc = run_balanced(pkv, d2, append=False)
     assert torch.equal(a, c) and torch.equal(la, lc)
     ref, _ = _oracle(orc, inp, kp, vp)

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, dev, to_dev
+from gpu_helpers import assert_close, dev, tables_to_dev, to_dev
 from synthetic import generate, generate_multiquery, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,8 @@ class Dev:
     def __init__(self, inp, kc, vc, ks, vs, kind):
         self.k, self.v = to_dev(kc), to_dev(vc)
         self.ks, self.vs = to_dev(ks), to_dev(vs)
-        self.bt, self.cl = to_dev(inp.block_tables), to_dev(inp.context_lens)
+        self.bt, self.cl = tables_to_dev(inp.block_tables, inp.context_lens,
+                                         inp.wl.block_size, kc.shape[0])
         self.q = to_dev(inp.query[0])
         self.k_new, self.v_new = to_dev(inp.k_new[0]), to_dev(inp.v_new[0])
         self.dt = _dtype(kind)
@@ -135,7 +136,8 @@ def test_multiquery(orc, pkv, kind):
     kc, vc, ks, vs = _caches(orc, base, kind)
     dt = _dtype(kind)
     k, v, kd, vd = to_dev(kc), to_dev(vc), to_dev(ks), to_dev(vs)
-    qs, bt, cl = to_dev(mq.query_start), to_dev(base.block_tables), to_dev(base.context_lens)
+    qs = to_dev(mq.query_start)
+    bt, cl = tables_to_dev(base.block_tables, base.context_lens, wl.block_size, kc.shape[0])
     max_q = int(mq.query_lens.max())
     pkv.paged_kv_write(to_dev(mq.k_rows[0]), to_dev(mq.v_rows[0]), qs, k, v, bt, cl, max_q,
                        k_scale=kd, v_scale=vd, kv_dtype=dt)
@@ -173,7 +175,8 @@ def test_int8_encode_exhaustive(orc, pkv, params):
     vc = np.zeros_like(kc)
     vbits = bits[::-1].copy()
     dk, dv = to_dev(kc), to_dev(vc)
-    pkv.paged_kv_append(to_dev(bits), to_dev(vbits), dk, dv, to_dev(tables), to_dev(ctx),
+    dbt, dcl = tables_to_dev(tables, ctx, bs, B)
+    pkv.paged_kv_append(to_dev(bits), to_dev(vbits), dk, dv, dbt, dcl,
                         k_scale=to_dev(prm), v_scale=to_dev(vprm), kv_dtype="int8")
     torch.cuda.synchronize()
     orc.append(bits, vbits, kc, vc, tables, ctx, bs, kv_dtype="int8", k_scale=prm,
@@ -216,7 +219,7 @@ def test_int8_full_size_sampled(orc, pkv):
     inp = generate(wl, groups=[0])
     kc, vc, ks, vs = _caches(orc, inp, "int8")
     k, v, kd, vd = to_dev(kc), to_dev(vc), to_dev(ks), to_dev(vs)
-    bt, cl = to_dev(inp.block_tables), to_dev(inp.context_lens)
+    bt, cl = tables_to_dev(inp.block_tables, inp.context_lens, wl.block_size, kc.shape[0])
     kw = dict(k_scale=kd, v_scale=vd, kv_dtype="int8")
     pkv.paged_kv_append(to_dev(inp.k_new[0]), to_dev(inp.v_new[0]), k, v, bt, cl, **kw)
     kp, vp = kc.copy(), vc.copy()

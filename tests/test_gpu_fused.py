@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, dev, fp8_group, to_dev
+from gpu_helpers import assert_close, dev, fp8_group, tables_to_dev, to_dev
 from synthetic import generate, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +74,8 @@ class Dev:
         self.k, self.v = to_dev(kc), to_dev(vc)
         self.ks = None if ks is None else to_dev(ks)
         self.vs = None if vs is None else to_dev(vs)
-        self.bt, self.cl = to_dev(inp.block_tables), to_dev(inp.context_lens)
+        self.bt, self.cl = tables_to_dev(inp.block_tables, inp.context_lens,
+                                         inp.wl.block_size, kc.shape[0])
         self.q = to_dev(inp.query[0])
         self.k_new, self.v_new = to_dev(inp.k_new[0]), to_dev(inp.v_new[0])
         self.kw = dict(k_scale=self.ks, v_scale=self.vs, kv_dtype=_dtype(kind))

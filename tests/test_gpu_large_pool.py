@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, dev, to_dev
+from gpu_helpers import assert_close, dev, tables_to_dev, to_dev
 from synthetic import bf16_bits_from_f32
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +88,7 @@ def test_bf16_pool_past_4gib(orc, pkv):
     k = _device_pool(x["k"], x["big"], nb, torch.int16)
     v = _device_pool(x["v"], x["big"], nb, torch.int16)
     q, kn, vn = to_dev(x["q"]), to_dev(x["kn"]), to_dev(x["vn"])
-    bt, cl = to_dev(x["far"]), to_dev(CTX)
+    bt, cl = tables_to_dev(x["far"], CTX, BS, nb)
 
     pkv.paged_kv_append(kn, vn, k, v, bt, cl)
     assert np.array_equal(_blocks(k, x["big"]).view(np.uint16), kc)
@@ -151,7 +151,7 @@ def test_fp8_pool_past_4gib(orc, pkv):
     vsd = torch.ones_like(ksd)
     ksd[idx], vsd[idx] = to_dev(ks), to_dev(vs)
     q, kn, vn = to_dev(x["q"]), to_dev(x["kn"]), to_dev(x["vn"])
-    bt, cl = to_dev(x["far"]), to_dev(CTX)
+    bt, cl = tables_to_dev(x["far"], CTX, BS, nb)
 
     ws = pkv.make_workspace(q, k)
     out = pkv.paged_append_decode_attention_balanced(q, kn, vn, k, v, bt, cl, scale,

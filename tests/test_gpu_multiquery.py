@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, bits16, dev, sample_rows, to_dev
+from gpu_helpers import assert_close, bits16, dev, sample_rows, tables_to_dev, to_dev
 from synthetic import bf16_bits_from_f32, generate_multiquery, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -42,8 +42,8 @@ class MQDevice:
         self.v_rows = to_dev(mq.v_rows[0])
         self.q = to_dev(mq.query[0])
         self.qs = to_dev(mq.query_start)
-        self.bt = to_dev(base.block_tables)
-        self.cl = to_dev(base.context_lens)
+        self.bt, self.cl = tables_to_dev(base.block_tables, base.context_lens,
+                                         base.wl.block_size, self.k.shape[0])
         self.ks = None if k_scale is None else to_dev(k_scale)
         self.vs = None if v_scale is None else to_dev(v_scale)
         self.max_q = max(1, int(mq.query_lens.max()))
@@ -202,7 +202,7 @@ def test_deterministic_and_placement_free(orc, pkv):
     tq = mq.base.block_tables.copy()
     tq[tq >= 0] = perm[tq[tq >= 0]]
     d2 = MQDevice(mq, k_pool=kq, v_pool=vq)
-    d2.bt = to_dev(tq)
+    d2.bt = tables_to_dev(tq, mq.base.context_lens, mq.base.wl.block_size, nb)[0]
     c, lc = run_mq(pkv, d2, write=False)
     assert torch.equal(a, c) and torch.equal(la, lc)
     ref, _ = oracle_mq(orc, mq, kp, vp)

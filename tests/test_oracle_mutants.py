@@ -17,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_formula.py", "tests/test_oracle_fp8.py",
         "tests/test_oracle_attention.py", "tests/test_oracle_multiquery.py",
-        "tests/test_oracle_blocks.py", "tests/test_oracle_quant.py"]
+        "tests/test_oracle_blocks.py", "tests/test_oracle_quant.py",
+        "tests/test_oracle_tables.py"]
 
 # (name, original text, planted text, occurrence count expected)
 MUTANTS = [
@@ -52,8 +53,22 @@ MUTANTS = [
      "slot = (t + 1) % block_size;\n        for (h = 0; h < Hkv; ++h) {"),
     ("append_swaps_k_v", "store_value(k_cache, k_scale, kv_dtype, dst, k_new[src], phys, h, Hkv);",
      "store_value(k_cache, k_scale, kv_dtype, dst, v_new[src], phys, h, Hkv);"),
-    ("block_scale_amax_over_all_slots", "for (slot = 0; slot < live[p]; ++slot)",
-     "for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)"),
+    ("block_scale_amax_over_all_slots",
+     "double amax = 0.0;\n            for (slot = 0; slot < live[p]; ++slot)",
+     "double amax = 0.0;\n            for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)"),
+    ("wide_scale_amax_over_all_slots",
+     "for (p = 0; p < num_blocks; ++p)\n            for (slot = 0; slot < live[p]; ++slot)",
+     "for (p = 0; p < num_blocks; ++p)\n            for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)"),
+    ("int8_params_over_all_slots",
+     "for (slot = 0; slot < live[p]; ++slot)\n                for (d = 0; d < D; ++d) {\n                    double v = orc_bf16_value(",
+     "for (slot = 0; slot < (live[p] ? block_size : 0); ++slot)\n                for (d = 0; d < D; ++d) {\n                    double v = orc_bf16_value("),
+    ("check_skips_partial_last_block",
+     "nblk = (T + block_size - 1) / block_size;\n        for (j = 0; j < nblk; ++j) {\n            int32_t p = block_tables",
+     "nblk = T / block_size;\n        for (j = 0; j < nblk; ++j) {\n            int32_t p = block_tables"),
+    ("check_pool_bound_inclusive", "if (p < 0 || p >= num_blocks)\n                return -(1 + b);",
+     "if (p < 0 || p > num_blocks)\n                return -(1 + b);"),
+    ("check_context_bound_strict", "(int64_t)T > (int64_t)max_blocks * block_size",
+     "(int64_t)T >= (int64_t)max_blocks * block_size"),
     ("split_range_overlaps", "int32_t t0 = s * split_tokens;",
      "int32_t t0 = s > 0 ? s * split_tokens - 1 : 0;"),
     ("mq_position_off_by_one", "int32_t p = T - q + i;", "int32_t p = T - q + i - 1;"),
