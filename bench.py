@@ -13,10 +13,16 @@ already resident in HBM.
 
 Prints ONE JSON line.  value = KV-read GB/s of the whole step (ideal KV
 bytes 2 * sum(ctx) * Hkv * D * bytes_per_elem per layer call, times the
-layers, / step time).  roofline = the attention call of every 8th timed
-step (layer i mod layers in step i), timed with HIP events on the stream
-it is launched on.  cpu_baseline = the CPU oracle on a bounded sample of the
-same workload, on this machine's host cores.
+layers, / step time), the step time being the host wall clock over exactly
+--steps steps bracketed by a device synchronisation on both sides.  The same
+timed region is also measured on the device, by two HIP events recorded on
+the stream the steps run on; roofline = the algorithmic bytes of one
+attention call over that device span per call (the call's merge or reduce
+launch included).  In the default run the line also carries the other
+target workloads (8B shape, 32k-token split context with a shared prefix,
+fp8 over 36 layers in 9 groups), each timed over at least 50 ms of steps,
+and the plain streaming-read probe's GB/s.  cpu_baseline = the CPU oracle on
+a bounded sample of the same workload, on this machine's host cores.
 """
 from __future__ import annotations
 
@@ -32,10 +38,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved KV-read GB/s (% of HBM peak) + decode tokens/s, paged decode attn 1 GPU"
 HBM_PEAK_GBS = 8000.0
-EVENT_STRIDE = 8             # timed steps per sampled attention launch
 MFMA_PEAK_TFLOPS = 2500.0    # dense bf16
 
 DEFAULT_WORKLOAD = "llama70b_b64_ragged1k_16k_bs32"
+# measured beside the headline in the default run: the 8B shape, the 32k
+# split-context workload with its shared prefix, and the fp8 36-layer step
+EXTRA_WORKLOADS = ("llama8b_b32_ctx4096_bs16", "llama70b_b4_ctx32k_split512_prefix2k",
+                   "fp8_36layers_groups4_b32_ctx2k_8k")
+MIN_TIMED_S = 0.05           # timed device work of each secondary workload
 
 
 def _args():
@@ -46,13 +56,14 @@ def _args():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--mode", default="auto",
                    choices=["auto", "balanced", "split", "single", "multiquery", "swap",
-                            "blockmanager"],
+                            "blockmanager", "stream"],
                    help="attention schedule: work-balanced, fixed splits + reduce, or one "
                         "wave per (sequence, kv head); auto = the workload's own split size "
                         "if it has one, multiquery if it has several new tokens per "
                         "sequence, else balanced; swap = whole-block moves of preempted "
                         "sequences to pinned host memory and back; blockmanager = host cost "
-                        "of the C++ block manager on a serving trace")
+                        "of the C++ block manager on a serving trace; stream = the plain "
+                        "streaming-read probe (4 GiB)")
     p.add_argument("--kv-format", default=None,
                    choices=["bf16", "fp8", "fp8_head", "fp8_tensor", "int8"],
                    help="cache format (default: the workload's own); fp8 = one scale per "
@@ -67,9 +78,11 @@ def _args():
     p.add_argument("--cold-steps", type=int, default=20,
                    help="extra event-timed steps, each after a 1 GiB write that evicts the "
                         "MALL and the L2s (cold_cache in the JSON line; 0 = skip)")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--cpu-seconds", type=float, default=24.0,
+                   help="target time of the single-threaded oracle baseline (3 runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="headline workload only (skip the other workloads and the probe)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -83,20 +96,74 @@ def main():
         print(f"bench.py: measures one GPU only (asked for --gpus {a.gpus}); "
               "the decode kernel has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    from synthetic import make_workload
 
-    import numpy as np
-    import torch
-
-    import paged_kv_cache_273_amd as pkv
-    from synthetic import generate, generate_multiquery, make_workload
-
+    if a.mode == "stream":
+        return print(json.dumps(_bench_stream(a)), flush=True)
     wl = make_workload(a.workload)
     if a.mode == "swap":
         return _bench_swap(a, wl)
     if a.mode == "blockmanager":
         return _bench_block_manager(a)
+    res = _run_workload(a, wl, a.mode, a.steps, a.warmup, a.cold_steps,
+                        cpu=not a.no_cpu_baseline, headline=True)
+    if a.workload == DEFAULT_WORKLOAD and a.mode == "auto" and not a.no_extra:
+        # the other target workloads, each timed over enough steps that the
+        # start and end of the timed region do not matter
+        res["configs"] = {}
+        for name in EXTRA_WORKLOADS:
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            res["configs"][name] = _run_workload(a, make_workload(name), "auto", None,
+                                                 a.warmup, a.cold_steps, cpu=False,
+                                                 headline=False)
+        res["hbm_stream_read"] = _bench_stream(a, summary=True)
+    print(json.dumps(res), flush=True)
+
+
+def _check_tables(tables, lens, block_size, num_blocks):
+    """The preconditions the kernels rely on (they are not checked on the
+    device): every sequence fits its table row and its live entries name
+    blocks of the pool."""
+    import numpy as np
+
+    nblk = (lens.astype(np.int64) + block_size - 1) // block_size
+    live = np.arange(tables.shape[1])[None, :] < nblk[:, None]
+    ok = (lens >= 0).all() and (nblk <= tables.shape[1]).all() and \
+        (((tables >= 0) & (tables < num_blocks)) | ~live).all()
+    if not ok:
+        raise SystemExit("bench.py: generated block tables break the kernel preconditions")
+
+
+def _timed(step, steps, warmup):
+    """warmup untimed steps, then `steps` steps bracketed by a device
+    synchronisation on both sides: host wall clock, and the device span
+    between two HIP events recorded on the stream the steps run on."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) * 1e-3
+
+
+def _run_workload(a, wl, mode_arg, steps, warmup, cold_steps, cpu, headline):
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_273_amd as pkv
+    from synthetic import generate, generate_multiquery
+
     multi = wl.q_uniform != (1, 1)
-    mode = a.mode
+    mode = mode_arg
     if mode == "auto":
         mode = "multiquery" if multi else ("split" if wl.split_tokens > 0 else "balanced")
     if (mode == "multiquery") != multi:
@@ -104,13 +171,14 @@ def main():
         sys.exit(2)
     S = 0
     if mode == "split":
-        S = a.split if a.split is not None else (wl.split_tokens or 512)
+        S = a.split if (a.split is not None and headline) else (wl.split_tokens or 512)
     dev = torch.device("cuda:0")
     t_gen = time.time()
     mq = generate_multiquery(wl) if multi else None
     inp = mq.base if multi else generate(wl)   # every cache group of the workload
     print(f"bench: generated {wl.name} in {time.time() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
+    _check_tables(inp.block_tables, inp.context_lens, wl.block_size, inp.num_blocks)
 
     def up(x):
         x = np.ascontiguousarray(x)
@@ -120,7 +188,7 @@ def main():
 
     live = torch.from_numpy(np.arange(wl.block_size)[None, :] < inp.live[:, None]).to(dev)
 
-    fmt = a.kv_format or wl.kv_dtype
+    fmt = (a.kv_format if headline else None) or wl.kv_dtype
     ebytes = 2 if fmt == "bf16" else 1
 
     def quant(src):
@@ -188,18 +256,11 @@ def main():
     if mode == "multiquery":
         ws = pkv.make_multiquery_workspace(qs[0], caches[0][0], max_q, kv_dtype=fmt)
 
-    # (start, end) HIP events around one attention call of every
-    # EVENT_STRIDE-th timed step (layer i % layers in step i, so every
-    # layer's call is sampled).  An event pair costs ~6 us of GPU time (two
-    # marker packets); recorded in every step it would be charged to every
-    # step, ~6% of a 90 us step.
-    ev = []
-
     # decode steps append in the attention launch of each group's first
     # layer (paged_append_decode_attention*), unless --unfused
-    fused = not multi and not a.unfused
+    fused = not multi and not (a.unfused and headline)
 
-    def step(record):
+    def step():
         for k, v, ks, vs, kn, vn in caches:
             if multi:
                 pkv.paged_kv_write(kn, vn, qstart, k, v, bt, cl, max_q, k_scale=ks, v_scale=vs,
@@ -210,12 +271,6 @@ def main():
             k, v, ks, vs, kn, vn = caches[layer // wl.layers_per_group]
             q = qs[layer]
             new = fused and layer % wl.layers_per_group == 0
-            timed = (record is not None and record % EVENT_STRIDE == 0
-                     and layer == record % wl.layers)
-            if timed:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
             if mode == "split" and new:
                 pkv.paged_append_decode_attention(q, kn, vn, k, v, bt, cl, scale,
                                                   split_tokens=S, partial_out=po,
@@ -243,33 +298,28 @@ def main():
             else:
                 pkv.paged_decode_attention(q, k, v, bt, cl, scale, out=out, k_scale=ks,
                                            v_scale=vs, kv_dtype=fmt)
-            if timed:
-                e1.record()
-                ev.append((e0, e1))
             if mode == "split":
                 pkv.split_context_reduce(po, pl, cl, S, out=out)
 
-    if a.calibrate_copy:
+    if a.calibrate_copy and headline:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(a.warmup):
-        step(None)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3 / len(ev)
-
-    step_s = wall / a.steps
+    if steps is None:
+        # secondary workloads: enough steps for MIN_TIMED_S of device time
+        _, est = _timed(step, 5, warmup)
+        steps = max(a.steps, int(math.ceil(MIN_TIMED_S / max(est / 5, 1e-6))))
+        warmup = 0
+    wall, span = _timed(step, steps, warmup)
+    step_s = wall / steps
+    dev_step_s = span / steps
+    call_s = dev_step_s / wl.layers           # one attention call (+ its merge / reduce)
     gbs = ideal / step_s / 1e9
-    kern_gbs = per_layer / kern_s / 1e9
-    cold = _cold_steps(step, a.cold_steps, ideal, dev) if a.cold_steps > 0 else None
+    kern_gbs = per_layer / call_s / 1e9
+    cold = _cold_steps(step, cold_steps, ideal, dev) if cold_steps > 0 else None
     # algorithmic flops of one attention call: q.k and p.v, 2 per multiply-add,
     # per (row or sequence, query head, visible token, head-dim element)
     if multi:
@@ -279,21 +329,63 @@ def main():
         visible = int(ctx.sum())
     flops = 4 * wl.Hq * wl.D * visible
     mfma_bound = flops / per_layer > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    kern_tflops = flops / kern_s / 1e12
-    traffic = _measured_traffic(a.traffic_json, f"{wl.name}:{mode}"
-                                + (f":{fmt}" if fmt != wl.kv_dtype else ""))
+    kern_tflops = flops / call_s / 1e12
+    key = f"{wl.name}:{mode}" + (f":{fmt}" if fmt != wl.kv_dtype else "")
+    traffic = _measured_traffic(a.traffic_json, key)
+    kernel = {"split": "decode_kernel (split) + reduce_kernel", "single": "decode_kernel",
+              "balanced": "decode_balanced_kernel + balanced_merge_kernel",
+              "multiquery": ("prefill_kernel" if mfma_bound else
+                             "decode_balanced_kernel (causal columns) + balanced_merge_kernel")
+              }[mode]
+    step_desc = ({"split": "paged_append_decode_attention(split) + split_context_reduce",
+                  "balanced": "paged_append_decode_attention_balanced (append + decode, "
+                              "then log-sum-exp merge of cut units)",
+                  "single": "paged_append_decode_attention"} if fused else {
+                 "split": "paged_kv_append + paged_decode_attention(split) + "
+                          "split_context_reduce",
+                 "balanced": "paged_kv_append + paged_decode_attention_balanced "
+                             "(decode + log-sum-exp merge of cut units)",
+                 "single": "paged_kv_append + paged_decode_attention",
+                 "multiquery": "paged_kv_write + paged_multiquery_attention (causal, "
+                               "log-sum-exp merge of cut units)"})[mode]
+    roofline = ({
+        "bound": "mfma", "kernel": kernel,
+        "achieved": round(kern_tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(kern_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+        "launch_us": round(call_s * 1e6, 2), "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": per_layer,
+    } if mfma_bound else {
+        "bound": "hbm", "kernel": kernel,
+        "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "launch_us": round(call_s * 1e6, 2), "algorithmic_bytes_per_launch": per_layer,
+    })
+    if not headline:
+        res = {
+            "schedule": mode, "kv_dtype": fmt, "split_tokens": S, "layers_per_step": wl.layers,
+            "steps": steps, "ms_per_step": round(step_s * 1e3, 4),
+            "device_ms_per_step": round(dev_step_s * 1e3, 4), "gbs": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "decode_tokens_per_s": round(wl.B / step_s, 1),
+            "ideal_kv_bytes_per_step": ideal, "step": step_desc, "roofline": roofline,
+            "traffic_over_algorithmic": (round(traffic / per_layer, 4) if traffic else None),
+            "cold_cache": cold,
+        }
+        del caches, qs, out, po, pl, ws
+        torch.cuda.empty_cache()
+        return res
 
-    cpu = None
-    if not a.no_cpu_baseline:
-        cpu = _cpu_baseline(inp, wl, a.cpu_seconds, mq, fmt)
+    cpu_res = None
+    if cpu:
+        cpu_res = _cpu_baseline(inp, wl, a.cpu_seconds, mq, fmt)
 
-    res = {
+    return {
         "metric": METRIC,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -303,6 +395,7 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(wl.B / step_s, 1),
         "new_tokens_per_s": round(rows / step_s, 1),
+        "device_ms_per_step": round(dev_step_s * 1e3, 4),
         "config": {
             "workload": wl.name, "batch": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
             "block_size": wl.block_size, "kv_dtype": fmt,
@@ -312,39 +405,13 @@ def main():
             "layers_per_step": wl.layers, "cache_groups": wl.groups,
             "new_tokens_per_sequence": (list(wl.q_uniform) if multi else 1),
             "new_tokens_per_step": rows,
-            "step": ({"split": "paged_append_decode_attention(split) + split_context_reduce",
-                      "balanced": "paged_append_decode_attention_balanced (append + decode, "
-                                  "then log-sum-exp merge of cut units)",
-                      "single": "paged_append_decode_attention"} if fused else {
-                     "split": "paged_kv_append + paged_decode_attention(split) + "
-                              "split_context_reduce",
-                     "balanced": "paged_kv_append + paged_decode_attention_balanced "
-                                 "(decode + log-sum-exp merge of cut units)",
-                     "single": "paged_kv_append + paged_decode_attention",
-                     "multiquery": "paged_kv_write + paged_multiquery_attention (causal, "
-                                   "log-sum-exp merge of cut units)"})[mode],
+            "step": step_desc,
         },
-        "roofline": ({
-            "bound": "mfma", "kernel": "prefill_kernel",
-            "achieved": round(kern_tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(kern_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
-            "launch_us": round(kern_s * 1e6, 2), "algorithmic_flops_per_launch": flops,
-            "algorithmic_bytes_per_launch": per_layer,
-        } if mfma_bound else {
-            "bound": "hbm",
-            "kernel": {"split": "decode_kernel (split)", "single": "decode_kernel",
-                       "balanced": "decode_balanced_kernel + balanced_merge_kernel",
-                       "multiquery": "decode_balanced_kernel (causal columns) + "
-                                     "balanced_merge_kernel"}[mode],
-            "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "launch_us": round(kern_s * 1e6, 2), "algorithmic_bytes_per_launch": per_layer,
-        }),
+        "roofline": roofline,
         "attention_tflops": round(kern_tflops, 2),
         "cold_cache": cold,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_res,
     }
-    print(json.dumps(res), flush=True)
 
 
 def _cold_steps(step, n, ideal, dev):
@@ -365,7 +432,7 @@ def _cold_steps(step, n, ideal, dev):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            step(None)
+            step()
             e1.record()
             pairs.append((e0, e1))
         torch.cuda.synchronize()
@@ -383,6 +450,56 @@ def _cold_steps(step, n, ideal, dev):
         "frac_median": round(ideal / (cold_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "warm_step_us_median_same_timing": round(warm_med, 2),
     }
+
+
+STREAM_BYTES = 1 << 32        # 4 GiB: 16x the MALL, so the probe reads HBM
+
+
+def _bench_stream(a, summary=False):
+    """The plain streaming-read probe (pkv_stream_read): a 4 GiB buffer read
+    once per launch by 1024 / 2048 / 4096 waves, each a contiguous chunk of
+    16-byte non-temporal loads; launches back to back, timed with one HIP
+    event pair around 10 of them after 3 untimed ones."""
+    import torch
+
+    import paged_kv_cache_273_amd as pkv
+
+    dev = torch.device("cuda:0")
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    out = {}
+    for waves in (1024, 2048, 4096):
+        run = lambda: pkv.pkv_stream_read(buf, waves, sink)   # noqa: E731
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 10
+        out[str(waves)] = round(STREAM_BYTES / t / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    best = max(out.values())
+    res = {"bytes": STREAM_BYTES, "gbs_by_waves": out, "best_gbs": best,
+           "best_frac_of_peak": round(best / HBM_PEAK_GBS, 4),
+           "probe": "pkv_stream_read: each wave one contiguous chunk, 16-byte non-temporal "
+                    "loads, 8 per lane in flight"}
+    if summary:
+        return res
+    return {"metric": "streaming-read GB/s of a plain HIP probe (4 GiB)", "value": best,
+            "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 3,
+            "ms_per_step": round(STREAM_BYTES / best / 1e6, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "stream read, 4 GiB"}, **res,
+            "roofline": {"bound": "hbm", "kernel": "stream_read_kernel", "achieved": best,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(best / HBM_PEAK_GBS, 4), "traffic": None},
+            "cpu_baseline": None}
 
 
 HOST_LINK_GBS = 64.0     # PCIe 5.0 x16, one direction
@@ -598,76 +715,91 @@ def _oracle_cache(oracle, kp, vp, inp, wl, fmt):
     return oracle.quantize_pool(kp, ks, fmt), oracle.quantize_pool(vp, vs, fmt), ks, vs
 
 
+def _host_threads():
+    """Host threads this process may use (its CPU affinity), at most 16: the
+    share of host cores that comes with one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _cpu_baseline(inp, wl, target_s, mq=None, fmt="bf16"):
-    """The oracle (single-threaded C, fp64) on whole sequences of the same
-    workload until about target_s seconds of CPU time; GB/s on the same
-    ideal-byte formula."""
-    if mq is not None:
-        return _cpu_baseline_multiquery(mq, target_s, fmt)
+    """The oracle (plain C, fp64) on whole sequences of the same workload:
+    single-threaded on a sample of about target_s / 3 seconds, and with one
+    host thread per sequence at a time on every host thread this process may
+    use, on as many sequences as that takes; each the median of 3 runs of
+    the same sample.  GB/s on the same ideal-byte formula; generation and
+    cache preparation are not timed."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
 
-    kind = fmt
-    kp, vp, ks, vs = _oracle_cache(oracle, inp.k_pool[0], inp.v_pool[0], inp, wl, fmt)
-    oracle.append(inp.k_new[0], inp.v_new[0], kp, vp, inp.block_tables, inp.context_lens,
-                  wl.block_size, kv_dtype=kind, k_scale=ks, v_scale=vs)
-    done_bytes = 0
-    seqs = 0
+    multi = mq is not None
+    base = mq.base if multi else inp
+    kp, vp, ks, vs = _oracle_cache(oracle, base.k_pool[0], base.v_pool[0], base, wl, fmt)
+    if multi:
+        oracle.write_tokens(mq.k_rows[0], mq.v_rows[0], mq.query_start, kp, vp,
+                            base.block_tables, base.context_lens, wl.block_size, kv_dtype=fmt,
+                            k_scale=ks, v_scale=vs)
+    else:
+        oracle.append(base.k_new[0], base.v_new[0], kp, vp, base.block_tables,
+                      base.context_lens, wl.block_size, kv_dtype=fmt, k_scale=ks, v_scale=vs)
+    ebytes = 2 if fmt == "bf16" else 1
+    seq_bytes = [2 * int(base.context_lens[b]) * wl.Hkv * wl.D * ebytes for b in range(wl.B)]
+    kw = dict(block_size=wl.block_size, Hkv=wl.Hkv, kv_dtype=fmt, k_scale=ks, v_scale=vs)
+
+    def one(b):
+        bt = np.ascontiguousarray(base.block_tables[b:b + 1])
+        cl = np.ascontiguousarray(base.context_lens[b:b + 1])
+        if multi:
+            r0, r1 = int(mq.query_start[b]), int(mq.query_start[b + 1])
+            oracle.multiquery_attention(np.ascontiguousarray(mq.query[0][r0:r1]),
+                                        np.array([0, r1 - r0], dtype=np.int32), kp, vp, bt, cl,
+                                        base.scale, **kw)
+        else:
+            oracle.paged_attention(np.ascontiguousarray(base.query[0][b:b + 1]), kp, vp, bt,
+                                   cl, base.scale, **kw)
+
+    # single thread: the first sequences, up to about target_s / 3 per run
     t0 = time.perf_counter()
-    for b in range(wl.B):
-        sl = slice(b, b + 1)
-        oracle.paged_attention(np.ascontiguousarray(inp.query[0][sl]), kp, vp,
-                               np.ascontiguousarray(inp.block_tables[sl]),
-                               np.ascontiguousarray(inp.context_lens[sl]), inp.scale,
-                               block_size=wl.block_size, Hkv=wl.Hkv, kv_dtype=kind,
-                               k_scale=ks, v_scale=vs)
-        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * (2 if fmt == "bf16" else 1)
-        seqs += 1
-        if time.perf_counter() - t0 >= target_s:
-            break
-    el = time.perf_counter() - t0
-    gbs = done_bytes / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{seqs} of {wl.B} sequences (all {wl.Hq} query heads, "
-                      f"{done_bytes / 1e6:.0f} MB of KV), single-threaded fp64 C, "
-                      f"{el:.1f} s; {seqs / el:.3f} sequences/s",
-            "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
+    n1 = 0
+    while n1 < wl.B and (n1 == 0 or time.perf_counter() - t0 < target_s / 3):
+        one(n1)
+        n1 += 1
+    runs1 = [time.perf_counter() - t0]
+    for _ in range(2):
+        t0 = time.perf_counter()
+        for b in range(n1):
+            one(b)
+        runs1.append(time.perf_counter() - t0)
+    single = sum(seq_bytes[:n1]) / sorted(runs1)[1] / 1e9
 
-
-def _cpu_baseline_multiquery(mq, target_s, fmt):
-    """The multi-query oracle on whole sequences."""
-    import numpy as np
-
-    import oracle
-
-    wl, inp = mq.wl, mq.base
-    kind = fmt
-    kp, vp, ks, vs = _oracle_cache(oracle, inp.k_pool[0], inp.v_pool[0], inp, wl, fmt)
-    oracle.write_tokens(mq.k_rows[0], mq.v_rows[0], mq.query_start, kp, vp, inp.block_tables,
-                        inp.context_lens, wl.block_size, kv_dtype=kind, k_scale=ks, v_scale=vs)
-    done_bytes = rows = seqs = 0
-    t0 = time.perf_counter()
-    for b in range(wl.B):
-        r0, r1 = int(mq.query_start[b]), int(mq.query_start[b + 1])
-        oracle.multiquery_attention(np.ascontiguousarray(mq.query[0][r0:r1]),
-                                    np.array([0, r1 - r0], dtype=np.int32), kp, vp,
-                                    np.ascontiguousarray(inp.block_tables[b:b + 1]),
-                                    np.ascontiguousarray(inp.context_lens[b:b + 1]), inp.scale,
-                                    block_size=wl.block_size, Hkv=wl.Hkv, kv_dtype=kind,
-                                    k_scale=ks, v_scale=vs)
-        done_bytes += 2 * int(inp.context_lens[b]) * wl.Hkv * wl.D * (2 if fmt == "bf16" else 1)
-        rows += r1 - r0
-        seqs += 1
-        if time.perf_counter() - t0 >= target_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{seqs} of {wl.B} sequences ({rows} new tokens, all {wl.Hq} query "
-                      f"heads, {done_bytes / 1e6:.0f} MB of KV), single-threaded fp64 C, "
-                      f"{el:.1f} s",
-            "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
+    # every host thread, one sequence each at a time, over about as much
+    # work per thread as the single-threaded sample
+    threads = _host_threads()
+    nm = min(wl.B, n1 * threads)
+    runs = []
+    with cf.ThreadPoolExecutor(threads) as ex:      # ctypes releases the GIL
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(one, range(nm)))
+            runs.append(time.perf_counter() - t0)
+    multi_gbs = sum(seq_bytes[:nm]) / sorted(runs)[1] / 1e9
+    what = "sequences" + (f" ({int(mq.query_start[nm])} new tokens)" if multi else "")
+    return {"value": round(multi_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nm} of {wl.B} {what}, all {wl.Hq} query heads, "
+                      f"{sum(seq_bytes[:nm]) / 1e6:.0f} MB of KV, one sequence per host "
+                      f"thread at a time on {threads} threads, median of 3 runs "
+                      f"({', '.join(f'{r:.2f}' for r in runs)} s); fp64 C",
+            "single_thread": {"value": round(single, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"first {n1} {what}, "
+                                        f"{sum(seq_bytes[:n1]) / 1e6:.0f} MB of KV, median "
+                                        f"of 3 runs ({', '.join(f'{r:.2f}' for r in runs1)} s)"},
+            "cpu_model": _cpu_model(), "host_threads_available": threads}
 
 
 def _cpu_model():

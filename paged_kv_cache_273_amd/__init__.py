@@ -42,7 +42,9 @@ EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append",
            "pkv_bm_append_batch", "pkv_bm_fork",
            "pkv_bm_release", "pkv_bm_take_copies", "pkv_bm_context_len", "pkv_bm_table",
-           "pkv_bm_export", "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru")
+           "pkv_bm_export", "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru",
+           # measurement probe (include/pkv_probe.h)
+           "pkv_stream_read")
 
 
 class PagedKVError(RuntimeError):
@@ -87,6 +89,8 @@ def _load(path=LIB_PATH):
         getattr(L, name).argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
     L.paged_kv_copy_blocks.restype = C.c_int
     L.paged_kv_copy_blocks.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
+    L.pkv_stream_read.restype = C.c_int
+    L.pkv_stream_read.argtypes = [P, C.c_int64, I, P, P]
     L.pkv_status_string.restype = C.c_char_p
     L.pkv_status_string.argtypes = [C.c_int]
     return L
@@ -301,12 +305,17 @@ def paged_decode_workspace_size(Hq, Hkv, D, block_size, kv_dtype=PKV_BF16) -> in
     return n
 
 
+WORKSPACE_COUNTER_BYTES = 65536   # PKV_WORKSPACE_COUNTER_BYTES of include/pagedkv.h
+
+
 def make_workspace(query, k_cache, kv_dtype=None) -> torch.Tensor:
-    """A device buffer large enough for paged_decode_attention_balanced."""
+    """A zero-filled device buffer large enough for
+    paged_decode_attention_balanced (its arrival counters must start at
+    zero; every call leaves them zero)."""
     B, Hq, D = query.shape
     n = paged_decode_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
                                     _kv_dtype(k_cache, kv_dtype))
-    return torch.empty(n, dtype=torch.uint8, device=query.device)
+    return torch.zeros(n, dtype=torch.uint8, device=query.device)
 
 
 def _balanced(name, query, new, k_cache, v_cache, block_tables, context_lens, scale, workspace,
@@ -412,11 +421,12 @@ def paged_multiquery_workspace_size(Hq, Hkv, D, block_size, max_query_len,
 
 
 def make_multiquery_workspace(query, k_cache, max_query_len, kv_dtype=None) -> torch.Tensor:
-    """A device buffer large enough for paged_multiquery_attention."""
+    """A zero-filled device buffer large enough for
+    paged_multiquery_attention."""
     _, Hq, D = query.shape
     n = paged_multiquery_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
                                         max_query_len, _kv_dtype(k_cache, kv_dtype))
-    return torch.empty(n, dtype=torch.uint8, device=query.device)
+    return torch.zeros(n, dtype=torch.uint8, device=query.device)
 
 
 def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_tables, context_lens,
@@ -542,3 +552,16 @@ def paged_kv_copy_blocks(k_cache, v_cache, src_ids, dst_ids, *, k_scale=None, v_
 def max_splits_for(max_context: int, split_tokens: int) -> int:
     """Number of partial slots a sequence of max_context tokens needs."""
     return max(1, (int(max_context) + split_tokens - 1) // split_tokens)
+
+
+def pkv_stream_read(buf, waves, sink, *, stream=None) -> None:
+    """Reads the device buffer `buf` once (streaming-read probe,
+    include/pkv_probe.h); sink: a device tensor of at least 256 bytes."""
+    if not isinstance(buf, torch.Tensor) or not isinstance(sink, torch.Tensor):
+        raise TypeError("buf and sink must be torch tensors")
+    if sink.numel() * sink.element_size() < 256:
+        raise ValueError("sink must hold at least 256 bytes")
+    _same_device(buf, sink=sink)
+    nbytes = buf.numel() * buf.element_size()
+    _check("pkv_stream_read", _lib.pkv_stream_read(_ptr(buf), nbytes, int(waves), _ptr(sink),
+                                                   _stream(stream)))

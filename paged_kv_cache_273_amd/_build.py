@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SO = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "append_reduce.hip", "blocks.hip",
-           "block_manager.cpp"]
+           "probe.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -10,6 +10,7 @@
 #include <unordered_map>
 
 #include "../../include/pagedkv.h"
+#include "../../include/pkv_probe.h"
 #include "pkv_kernels.hpp"
 
 namespace {
@@ -296,23 +297,29 @@ static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t k
     return resident_groups(Hkv, D, block_size, kv_dtype, 0);
 }
 
-// Partial slots (2 per work-group) of rows_per_group rows, then the cut
-// records at the next 16-byte boundary.
+// The arrival counters (kCounterBytes, one per work-group and kv head of
+// the group), then the partial slots (2 per work-group) of rows_per_group
+// rows of D floats, then their lse values.
 static int64_t schedule_bytes(int ngroups, int64_t rows_per_group, int32_t D)
 {
     const int64_t rows = (int64_t)2 * ngroups * rows_per_group;
-    const int64_t parts = rows * (D + 1) * (int64_t)sizeof(float);
-    return (parts + 15) / 16 * 16 + (int64_t)ngroups * sizeof(pkv::CutRecord);
+    return pkv::kCounterBytes + rows * (D + 1) * (int64_t)sizeof(float);
 }
 
 static void carve_workspace(pkv::BalanceArgs& ws, void* workspace, int64_t rows_per_group,
                             int32_t D)
 {
     const int64_t rows = (int64_t)2 * ws.ngroups_launched * rows_per_group;
-    ws.part_out = (float*)workspace;
+    ws.counters = (int*)workspace;
+    ws.part_out = (float*)((char*)workspace + pkv::kCounterBytes);
     ws.part_lse = ws.part_out + (size_t)rows * D;
-    const int64_t parts = rows * (D + 1) * (int64_t)sizeof(float);
-    ws.cuts = (pkv::CutRecord*)((char*)workspace + (parts + 15) / 16 * 16);
+}
+
+// Whether the counters of n launched work-groups of head_group kv heads fit
+// the workspace's counter area.
+static bool counters_fit(int n, int head_group)
+{
+    return (int64_t)n * head_group * (int64_t)sizeof(int) <= pkv::kCounterBytes;
 }
 
 static int64_t balanced_bytes(int ngroups, int32_t Hkv, int32_t G, int32_t D, int kvf)
@@ -407,6 +414,8 @@ static int balanced_call(const uint16_t* query, const uint16_t* k_new, const uin
     // read whole at one time (measured ~1% faster than a range per group)
     ws.head_split = pkv::balanced_one_group_per_cu(Hkv, 0, fmt.kvf) ? Hkv / ws.head_group : 1;
     ws.ngroups_launched = n / ws.head_split * ws.head_split;
+    if (!counters_fit(ws.ngroups_launched, ws.head_group))
+        return PKV_EUNSUPPORTED;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * G, D);
     // range boundaries are computed in double precision: keep
     // (tiles of the call) * (groups launched) below 2^52
@@ -610,6 +619,8 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     ws.head_group = pkv::balanced_head_group(Hkv, nct, fmt.kvf);
     ws.head_split = 1;
     ws.ngroups_launched = n;
+    if (!counters_fit(ws.ngroups_launched, ws.head_group))
+        return PKV_EUNSUPPORTED;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * 16 * nct, D);
     // range boundaries in double precision: (tiles of the call) * (groups
     // launched) must stay below 2^52
@@ -762,6 +773,16 @@ int split_context_reduce(const float* partial_out, const float* partial_lse,
     a.split_tokens = split_tokens;
     a.max_splits = max_splits;
     return launched(pkv::launch_reduce(a, (hipStream_t)stream));
+}
+
+int pkv_stream_read(const void* buf, int64_t bytes, int32_t waves, uint32_t* sink,
+                    void* stream)
+{
+    if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4))
+        return PKV_EINVAL;
+    if (waves <= 0 || waves % 4 != 0 || bytes <= 0 || bytes % ((int64_t)waves * 8192) != 0)
+        return PKV_EINVAL;
+    return launched(pkv::launch_stream_read(buf, bytes, waves, sink, (hipStream_t)stream));
 }
 
 } // extern "C"

@@ -126,3 +126,37 @@ def sample_rows(B, Hq, n, seed=0):
     while len(rows) < min(n, B * Hq):
         rows.add((int(rng.integers(B)), int(rng.integers(Hq))))
     return sorted(rows)
+
+
+def host_threads():
+    """Host threads for the oracle (this process's CPU affinity, at most 16)."""
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_rows(orc, query, kp, vp, tables, lens, scale, *, block_size, Hkv, kv_dtype="bf16",
+                ks=None, vs=None, rows=None):
+    """Oracle output and lse of every (sequence, query head) row (or of the
+    listed rows), one row per task on a pool of host threads (the oracle's
+    ctypes calls release the GIL).  Returns out [n, D], lse [n] in row order
+    and the row list."""
+    import concurrent.futures as cf
+
+    B, Hq, D = query.shape
+    if rows is None:
+        rows = [(b, hq) for b in range(B) for hq in range(Hq)]
+
+    def one(r):
+        b, hq = r
+        return orc.attend_range(query, kp, vp, tables, b, hq, 0, int(lens[b]), scale,
+                                block_size=block_size, Hkv=Hkv, kv_dtype=kv_dtype,
+                                k_scale=ks, v_scale=vs)
+
+    with cf.ThreadPoolExecutor(host_threads()) as ex:
+        res = list(ex.map(one, rows, chunksize=8))
+    return np.stack([o for o, _ in res]), np.array([l for _, l in res]), rows

@@ -35,7 +35,8 @@ def _res(v):
     return F() + v[1] if isinstance(v, tuple) and v and v[0] == "buf" else v
 
 
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pagedkv.h", "pkv_block_manager.h")]
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in ("pagedkv.h", "pkv_block_manager.h", "pkv_probe.h")]
 
 
 def _declared(headers=HEADERS):
@@ -72,12 +73,29 @@ def test_header_declares_the_boundary():
 
 
 def test_block_manager_header_declares_its_calls():
-    names = _declared(HEADERS[1:])
+    names = _declared(HEADERS[1:2])
     assert names == sorted(["pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append",
                             "pkv_bm_append_batch",
                             "pkv_bm_fork", "pkv_bm_release", "pkv_bm_take_copies",
                             "pkv_bm_context_len", "pkv_bm_table", "pkv_bm_export",
                             "pkv_bm_stats", "pkv_bm_ref", "pkv_bm_lru"]), names
+
+
+def test_probe_header_declares_its_call():
+    assert _declared(HEADERS[2:]) == ["pkv_stream_read"]
+
+
+def test_stream_read_rejects(pkv):
+    L = pkv.lib()
+    f = F()
+    assert L.pkv_stream_read(None, 1 << 20, 128, f, None) == -1
+    assert L.pkv_stream_read(f + 8, 1 << 20, 128, f, None) == -1     # misaligned buffer
+    assert L.pkv_stream_read(f, 1 << 20, 128, None, None) == -1      # no sink
+    assert L.pkv_stream_read(f, 1 << 20, 0, f, None) == -1
+    assert L.pkv_stream_read(f, 1 << 20, 6, f, None) == -1           # not a multiple of 4
+    assert L.pkv_stream_read(f, 1 << 20, 256, f, None) == -1         # 4 KB per wave
+    assert L.pkv_stream_read(f, (1 << 20) + 16, 128, f, None) == -1
+    assert L.pkv_stream_read(f, 0, 128, f, None) == -1
 
 
 def test_library_exports_every_declared_symbol(pkv):
