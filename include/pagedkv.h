@@ -106,13 +106,6 @@ enum pkv_dtype {
 /* Supported shapes of this build: D in {64, 128}; block_size in {16, 32};
  * 1 <= Hq / Hkv <= 16; Hq % Hkv == 0. */
 
-/* The first PKV_WORKSPACE_COUNTER_BYTES bytes of a workspace of the
- * balanced and multi-query calls hold arrival counters: they must be zero
- * before the first call that uses the workspace (zero-fill it once when it
- * is allocated), and every call leaves them zero again.  The rest of the
- * workspace is scratch whose contents on entry do not matter. */
-#define PKV_WORKSPACE_COUNTER_BYTES 65536
-
 /*
  * paged_kv_append -- write the decode step's new K and V rows into the cache.
  *
@@ -231,23 +224,18 @@ int split_context_reduce(const float* partial_out, const float* partial_lse,
  * together; every group starts at once: one group per compute unit for
  * four-head groups of bf16 / fp8 caches, as many as fit otherwise); a
  * pair cut by range boundaries is finished by a log-sum-exp merge of its
- * pieces, done in the same launch by the last of its pieces to finish
- * (one kernel launch per call).
+ * pieces (second launch, same stream).
  *
- *  workspace       : device memory of at least workspace_bytes, 16-byte
- *                    aligned, owned by the caller.  Its first
- *                    PKV_WORKSPACE_COUNTER_BYTES must be zero before its
- *                    first use and are left zero by every call; the rest is
- *                    scratch (contents on entry irrelevant, on return
- *                    unspecified).  Calls that share one workspace must be
- *                    ordered on one stream.
+ *  workspace       : device scratch of at least workspace_bytes, 16-byte
+ *                    aligned, owned by the caller; its contents on entry are
+ *                    irrelevant and on return unspecified.  Calls that share
+ *                    one workspace must be ordered on one stream.
  *  workspace_bytes : >= paged_decode_workspace_size(Hq, Hkv, D, block_size,
  *                    kv_dtype) for the device current at the call.
  *  out, lse_out    : as in single-pass paged_decode_attention (T == 0 gives
  *                    out = 0, lse = -inf).
  *  Returns PKV_EINVAL if the workspace is too small; PKV_EUNSUPPORTED if
- *  max_blocks * block_size exceeds 2^25 tokens or the device holds more
- *  work-groups than the counter area counts.
+ *  max_blocks * block_size exceeds 2^25 tokens.
  */
 int paged_decode_attention_balanced(const uint16_t* query,
                                     const void* k_cache, const void* v_cache,
@@ -371,11 +359,9 @@ int paged_kv_write(const uint16_t* k_rows, const uint16_t* v_rows,
  *
  *  query          : [total_rows, Hq, D] bf16 bits (device, 16-byte aligned).
  *  query_start    : [B + 1] int32 (device); total_rows, max_query_len host.
- *  workspace      : device memory of >= workspace_bytes, 16-byte aligned,
- *                   caller-owned; its first PKV_WORKSPACE_COUNTER_BYTES zero
- *                   before first use (left zero by every call), the rest
- *                   scratch; calls that share one must be ordered on one
- *                   stream.
+ *  workspace      : device scratch of >= workspace_bytes, 16-byte aligned,
+ *                   caller-owned, contents on entry irrelevant; calls that
+ *                   share one must be ordered on one stream.
  *  workspace_bytes: >= paged_multiquery_workspace_size(Hq, Hkv, D,
  *                   block_size, kv_dtype, max_query_len).
  *  out            : [total_rows, Hq, D] float; lse_out [total_rows, Hq]

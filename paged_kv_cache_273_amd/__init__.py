@@ -305,17 +305,12 @@ def paged_decode_workspace_size(Hq, Hkv, D, block_size, kv_dtype=PKV_BF16) -> in
     return n
 
 
-WORKSPACE_COUNTER_BYTES = 65536   # PKV_WORKSPACE_COUNTER_BYTES of include/pagedkv.h
-
-
 def make_workspace(query, k_cache, kv_dtype=None) -> torch.Tensor:
-    """A zero-filled device buffer large enough for
-    paged_decode_attention_balanced (its arrival counters must start at
-    zero; every call leaves them zero)."""
+    """A device buffer large enough for paged_decode_attention_balanced."""
     B, Hq, D = query.shape
     n = paged_decode_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
                                     _kv_dtype(k_cache, kv_dtype))
-    return torch.zeros(n, dtype=torch.uint8, device=query.device)
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
 
 
 def _balanced(name, query, new, k_cache, v_cache, block_tables, context_lens, scale, workspace,
@@ -421,12 +416,11 @@ def paged_multiquery_workspace_size(Hq, Hkv, D, block_size, max_query_len,
 
 
 def make_multiquery_workspace(query, k_cache, max_query_len, kv_dtype=None) -> torch.Tensor:
-    """A zero-filled device buffer large enough for
-    paged_multiquery_attention."""
+    """A device buffer large enough for paged_multiquery_attention."""
     _, Hq, D = query.shape
     n = paged_multiquery_workspace_size(Hq, k_cache.shape[2], D, k_cache.shape[1],
                                         max_query_len, _kv_dtype(k_cache, kv_dtype))
-    return torch.zeros(n, dtype=torch.uint8, device=query.device)
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
 
 
 def paged_multiquery_attention(query, query_start, k_cache, v_cache, block_tables, context_lens,

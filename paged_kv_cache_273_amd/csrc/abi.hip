@@ -297,29 +297,23 @@ static int balanced_groups(int32_t Hkv, int32_t D, int32_t block_size, int32_t k
     return resident_groups(Hkv, D, block_size, kv_dtype, 0);
 }
 
-// The arrival counters (kCounterBytes, one per work-group and kv head of
-// the group), then the partial slots (2 per work-group) of rows_per_group
-// rows of D floats, then their lse values.
+// Partial slots (2 per work-group) of rows_per_group rows, then the cut
+// records at the next 16-byte boundary.
 static int64_t schedule_bytes(int ngroups, int64_t rows_per_group, int32_t D)
 {
     const int64_t rows = (int64_t)2 * ngroups * rows_per_group;
-    return pkv::kCounterBytes + rows * (D + 1) * (int64_t)sizeof(float);
+    const int64_t parts = rows * (D + 1) * (int64_t)sizeof(float);
+    return (parts + 15) / 16 * 16 + (int64_t)ngroups * sizeof(pkv::CutRecord);
 }
 
 static void carve_workspace(pkv::BalanceArgs& ws, void* workspace, int64_t rows_per_group,
                             int32_t D)
 {
     const int64_t rows = (int64_t)2 * ws.ngroups_launched * rows_per_group;
-    ws.counters = (int*)workspace;
-    ws.part_out = (float*)((char*)workspace + pkv::kCounterBytes);
+    ws.part_out = (float*)workspace;
     ws.part_lse = ws.part_out + (size_t)rows * D;
-}
-
-// Whether the counters of n launched work-groups of head_group kv heads fit
-// the workspace's counter area.
-static bool counters_fit(int n, int head_group)
-{
-    return (int64_t)n * head_group * (int64_t)sizeof(int) <= pkv::kCounterBytes;
+    const int64_t parts = rows * (D + 1) * (int64_t)sizeof(float);
+    ws.cuts = (pkv::CutRecord*)((char*)workspace + (parts + 15) / 16 * 16);
 }
 
 static int64_t balanced_bytes(int ngroups, int32_t Hkv, int32_t G, int32_t D, int kvf)
@@ -414,8 +408,6 @@ static int balanced_call(const uint16_t* query, const uint16_t* k_new, const uin
     // read whole at one time (measured ~1% faster than a range per group)
     ws.head_split = pkv::balanced_one_group_per_cu(Hkv, 0, fmt.kvf) ? Hkv / ws.head_group : 1;
     ws.ngroups_launched = n / ws.head_split * ws.head_split;
-    if (!counters_fit(ws.ngroups_launched, ws.head_group))
-        return PKV_EUNSUPPORTED;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * G, D);
     // range boundaries are computed in double precision: keep
     // (tiles of the call) * (groups launched) below 2^52
@@ -619,8 +611,6 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     ws.head_group = pkv::balanced_head_group(Hkv, nct, fmt.kvf);
     ws.head_split = 1;
     ws.ngroups_launched = n;
-    if (!counters_fit(ws.ngroups_launched, ws.head_group))
-        return PKV_EUNSUPPORTED;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * 16 * nct, D);
     // range boundaries in double precision: (tiles of the call) * (groups
     // launched) must stay below 2^52

@@ -105,24 +105,14 @@ struct Cfg {
     static_assert(16 % V_RPI == 0, "a V load must stay inside one 16-token block");
 };
 
-// LDS slice of one wave: the V staging tiles (one per tile of a step), plus
-// the Q operands when a wave has several column tiles (their registers
-// would not fit beside the accumulators and the tiles in flight; each lane
-// reads back only what it wrote, so the slice needs no barrier).
-template <int D, int KVF, int NCT, int TPS = 1>
+// LDS slice of one wave: the V staging tile, plus the Q operands when a
+// wave has several column tiles (their registers would not fit beside the
+// accumulators and the tile in flight; each lane reads back only what it
+// wrote, so the slice needs no barrier).
+template <int D, int KVF, int NCT>
 constexpr int wave_lds_bytes()
 {
-    return TPS * Cfg<D, KVF>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, KVF>::Q_BYTES : 0);
-}
-
-// 32-token tiles per pipeline step of the balanced decode: two for fp8
-// caches, whose tile (8 KB at D = 128) is half a bf16 one, so a wave keeps
-// as many bytes in flight as a bf16 wave in the same registers; one
-// otherwise.
-template <int KVF, bool MQ>
-constexpr int balanced_tps()
-{
-    return (!MQ && KVF == 1) ? 2 : 1;
+    return Cfg<D, KVF>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, KVF>::Q_BYTES : 0);
 }
 
 // First of the 8 consecutive head-dim elements that lane group q feeds to
@@ -245,11 +235,8 @@ struct NoSegments {
 // tiles (consecutive context splits); at each segment end but the last,
 // emit(segment, r) takes the segment's finished state and r restarts,
 // while the next segment's first tile is already streaming in.  The last
-// segment's state is left in r as for a single range.  TPS > 1: a pipeline
-// step covers TPS consecutive tiles, all loaded together (more bytes in
-// flight per wave for 1-byte caches); no causal columns or segments then.
-template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL, int TPS = 1,
-          typename Emit = NoSegments>
+// segment's state is left in r as for a single range.
+template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL, typename Emit = NoSegments>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
                                              int h, int t_begin, int t_end,
                                              const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT],
@@ -269,7 +256,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     // dead); in registers for one column tile, in LDS for several.
     constexpr bool QLDS = NCT > 1;
     typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
-    lds_u32x4* qlds = (lds_u32x4*)(lds + TPS * C::LDS_BYTES);
+    lds_u32x4* qlds = (lds_u32x4*)(lds + C::LDS_BYTES);
     bf16x8 qf[QLDS ? 1 : NCT][C::KSTEPS];
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
@@ -421,8 +408,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     const float sl2 = a.scale_log2;
 
     // V rows -> LDS as bf16 (zeroed past the range end).
-    auto stage_v = [&](int t0, const TileAddr& ta, const Tile<D, KVF>& tl, bool masked,
-                       unsigned char* vl) {
+    auto stage_v = [&](int t0, const TileAddr& ta, const Tile<D, KVF>& tl, bool masked) {
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
             const int rr = k * C::V_RPI + lane / C::V_LPR;
@@ -441,13 +427,13 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                     lo = u32x4{0u, 0u, 0u, 0u};
                     hi = u32x4{0u, 0u, 0u, 0u};
                 }
-                u32x2* dst = (u32x2*)(vl + rr * C::PITCH + 32 * c);
+                u32x2* dst = (u32x2*)(lds + rr * C::PITCH + 32 * c);
                 dst[0] = u32x2{lo[0], lo[1]};
                 dst[1] = u32x2{lo[2], lo[3]};
                 dst[2] = u32x2{hi[0], hi[1]};
                 dst[3] = u32x2{hi[2], hi[3]};
             } else {
-                u32x2* dst = (u32x2*)(vl + rr * C::PITCH + 16 * c);
+                u32x2* dst = (u32x2*)(lds + rr * C::PITCH + 16 * c);
                 dst[0] = u32x2{v[0], v[1]};
                 dst[1] = u32x2{v[2], v[3]};
             }
@@ -485,7 +471,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
 
     // online softmax update and O^T += V^T . P^T from the staged V rows
     auto softmax_pv = [&](int t0, const TileAddr& ta, const f32x4 (&sacc)[NCT][2],
-                          bool masked, const unsigned char* vl) {
+                          bool masked) {
         bf16x8 pb[NCT], pb_lo[NCT];
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
@@ -550,7 +536,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             pb_lo[j] = as_bf16x8(pr);
         }
 
-        const unsigned short* l16 = (const unsigned short*)vl;
+        const unsigned short* l16 = (const unsigned short*)lds;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             u32x4 vw;
@@ -574,67 +560,6 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     // while this tile's softmax and PV product run.  Tiles that end at or
     // before every column's limit skip the causal mask.
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-    if constexpr (TPS > 1) {
-        static_assert(!CAUSAL, "several tiles per step only without causal columns");
-        // A step covers tiles TPS*it .. TPS*it + TPS - 1; its V loads are
-        // issued right after the previous step's V tiles are staged, each
-        // tile's K loads right after that tile's scores.  The last step may
-        // hold tiles past the range end: they were loaded from the clamped
-        // last block (in bounds) and are skipped.
-        const int nsteps = (ntiles + TPS - 1) / TPS;
-        Tile<D, KVF> tl[TPS];
-        TileAddr ta[TPS];
-#pragma unroll
-        for (int s = 0; s < TPS; ++s)
-            ta[s] = tile_addr(t_begin + kTile * s);
-        if (append_last && nsteps == 1)
-            stores_before_loads();
-#pragma unroll
-        for (int s = 0; s < TPS; ++s) {
-            load_k(ta[s], tl[s]);
-            load_v(ta[s], tl[s]);
-        }
-        auto tps_step = [&](int it, bool last) {
-            const int t0 = t_begin + kTile * TPS * it;
-            TileAddr tn[TPS];
-            if (!last) {
-#pragma unroll
-                for (int s = 0; s < TPS; ++s)
-                    tn[s] = tile_addr(t0 + kTile * (TPS + s));
-            }
-#pragma unroll
-            for (int s = 0; s < TPS; ++s)
-                if (!last || t0 + kTile * s < t_end)
-                    stage_v(t0 + kTile * s, ta[s], tl[s], last, lds + s * C::LDS_BYTES);
-            if (!last) {
-                if (append_last && it == nsteps - 2)
-                    stores_before_loads();         // the next step holds slot t_end - 1
-#pragma unroll
-                for (int s = 0; s < TPS; ++s)
-                    load_v(tn[s], tl[s]);
-            }
-#pragma unroll
-            for (int s = 0; s < TPS; ++s) {
-                if (last && t0 + kTile * s >= t_end)
-                    continue;                      // a tile past the range end
-                f32x4 sacc[NCT][2];
-                qk(ta[s], tl[s], sacc);
-                if (!last)
-                    load_k(tn[s], tl[s]);
-                softmax_pv(t0 + kTile * s, ta[s], sacc, last, lds + s * C::LDS_BYTES);
-            }
-            if (!last) {
-#pragma unroll
-                for (int s = 0; s < TPS; ++s)
-                    ta[s] = tn[s];
-            }
-        };
-        for (int it = 0; it < nsteps - 1; ++it)
-            tps_step(it, false);
-        tps_step(nsteps - 1, true);
-        apply_fold();
-        return;
-    }
     int n_plain = ntiles - 1;
     if (CAUSAL)
         n_plain = max(0, min(n_plain, (min(t_end, cs.mask_from) - t_begin) / kTile));
@@ -647,14 +572,14 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     auto step = [&](int it, bool masked) {
         const int t0 = t_begin + kTile * it;
         const TileAddr tn = tile_addr(t0 + kTile);
-        stage_v(t0, ta, tl, false, lds);
+        stage_v(t0, ta, tl, false);
         if (append_last && it == ntiles - 2)
             stores_before_loads();             // tile tn holds slot t_end - 1
         load_v(tn, tl);
         f32x4 sacc[NCT][2];
         qk(ta, tl, sacc);
         load_k(tn, tl);
-        softmax_pv(t0, ta, sacc, masked, lds);
+        softmax_pv(t0, ta, sacc, masked);
         ta = tn;
         if (seg_tiles > 0 && (it + 1) % seg_tiles == 0) {   // a segment ends here
             apply_fold();
@@ -669,10 +594,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             step(it, true);
     {
         const int t0 = t_begin + kTile * (ntiles - 1);
-        stage_v(t0, ta, tl, true, lds);
+        stage_v(t0, ta, tl, true);
         f32x4 sacc[NCT][2];
         qk(ta, tl, sacc);
-        softmax_pv(t0, ta, sacc, true, lds);
+        softmax_pv(t0, ta, sacc, true);
     }
     apply_fold();
 }
@@ -802,10 +727,9 @@ void decode_kernel(DecodeArgs a)
 // whatever the mix of context lengths.  A unit inside one group's range is
 // written straight to `out`; a unit cut by range boundaries leaves one
 // normalised partial per piece in the workspace (slot 2r for a group's
-// first piece, 2r+1 for its last), and the last of its pieces to finish
-// merges them with the log-sum-exp rule in the same launch (arrival
-// counters, device-coherent partials: no second launch and no cache
-// write-back).
+// first piece, 2r+1 for its last), the group holding its first piece
+// records it (CutRecord), and balanced_merge_kernel combines the pieces of
+// every recorded unit with the log-sum-exp rule.
 //
 // Several new tokens per sequence (MQ): the columns of kv head h are the
 // pairs (new row i, head g) in the order c = i * G + g, cut into column
@@ -842,6 +766,18 @@ template <bool MQ>
 __device__ __forceinline__ long long wave_sum_w(long long v)
 {
     return MQ ? wave_sum_ll(v) : (long long)wave_sum_i((int)v);
+}
+
+// sum over sequences [0, b_end) of seq_tiles (same value in every lane)
+template <bool MQ, int NCT>
+__device__ __forceinline__ long long tiles_before(const DecodeArgs& a, int b_end)
+{
+    long long s = 0;
+    for (int c = 0; c < b_end; c += kWave) {
+        const int b = c + __lane_id();
+        s += wave_sum_w<MQ>(b < b_end ? seq_tiles<MQ, NCT>(a, b) : 0);
+    }
+    return s;
 }
 
 // Sequence whose units contain linear tile x of the (b, unit, tile) list
@@ -899,138 +835,6 @@ __device__ __forceinline__ long long range_of(long long x, long long total, long
     return r;
 }
 
-// Where the pieces of a cut unit live: the unit's tiles span ranges rf..rl
-// (one piece per range, every range non-empty); the piece in range r sits
-// in partial slot 2 * (r * NS + hs) + 1 if it is not the first piece of its
-// range (only range rf can start before the unit), else in slot
-// 2 * (r * NS + hs).
-struct CutUnit {
-    long long ustart, total, R, rf, rl;
-    int NS, hs, rows_per_slot;
-};
-
-__device__ __forceinline__ long long piece_slot(const CutUnit& u, long long r)
-{
-    const bool second = r == u.rf && range_start(r, u.total, u.R) < u.ustart;
-    return 2 * (r * u.NS + u.hs) + (second ? 1 : 0);
-}
-
-// Stores this wave's piece of a cut unit as normalised partial rows and
-// their lse (device-coherent).  in_row: the wave's first row in a slot; the
-// row of column tile j, lane column r16, is in_row + 16 j + r16.
-template <int D, int NCT>
-__device__ __forceinline__ void store_cut_piece(const BalanceArgs& ws, const CutUnit& u,
-                                                long long r, int in_row,
-                                                const RangeAcc<D> (&acc)[NCT],
-                                                const bool (&live)[NCT])
-{
-    const int q4 = __lane_id() >> 4;
-    const int r16 = __lane_id() & 15;
-    const long long own = piece_slot(u, r) * u.rows_per_slot + in_row + r16;
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-        float inv, lse;
-        finish_range<D>(acc[j], inv, lse);
-        if (!live[j])
-            continue;
-        float* o = ws.part_out + (own + 16 * j) * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-            store_coherent(o + 16 * dt + 4 * q4, acc[j].acc[dt] * inv);
-        if (q4 == 0)
-            store_coherent_f32(ws.part_lse + own + 16 * j, lse);
-    }
-}
-
-// Counts this wave's stored piece of a cut unit in the unit's arrival
-// counter; the last of the unit's pieces to arrive merges them all
-// (log-sum-exp rule, pieces in range order, so the result does not depend
-// on which piece arrives last), writes the output rows (orow / lrow per
-// live column) and resets the counter for the next call.  Called once the
-// wave has no loads in flight.
-template <int D, int NCT>
-__device__ __forceinline__ void arrive_and_merge(const BalanceArgs& ws, const CutUnit& u,
-                                                 int* counter, int in_row,
-                                                 const bool (&live)[NCT],
-                                                 float* const (&orow)[NCT],
-                                                 float* const (&lrow)[NCT])
-{
-    constexpr int DT = D / 16;
-    const int q4 = __lane_id() >> 4;
-    const int r16 = __lane_id() & 15;
-    if (arrive(counter) != (int)(u.rl - u.rf))
-        return;                                  // a later piece will merge
-
-    // every piece is loaded back, one column tile at a time, kMB pieces in
-    // flight (more would spill registers)
-    constexpr int kMB = 2;
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-        float m = -__builtin_inff();
-        float wsum = 0.f;
-        f32x4 o[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (long long base = u.rf; base <= u.rl; base += kMB) {
-            f32x4 v[kMB][DT];
-            float l[kMB];
-#pragma unroll
-            for (int k = 0; k < kMB; ++k) {
-                const long long rr = base + k;
-                l[k] = -__builtin_inff();
-                // a dead column's lane has no row of its own in the slot (for
-                // G < 16 its index runs past the wave's rows)
-                if (rr > u.rl || !live[j])
-                    continue;
-                const long long row = piece_slot(u, rr) * u.rows_per_slot + in_row + 16 * j + r16;
-                l[k] = load_coherent_f32(ws.part_lse + row);
-                const float* src = ws.part_out + row * D + 4 * q4;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    v[k][dt] = load_coherent(src + 16 * dt);
-            }
-#pragma unroll
-            for (int k = 0; k < kMB; ++k) {
-                // a piece in which the column sees nothing carries no weight
-                if (l[k] == -__builtin_inff())
-                    continue;
-                const float m_new = fmaxf(m, l[k]);
-                const float c = __expf(m - m_new);               // m = -inf: 0
-                const float e = __expf(l[k] - m_new);
-                wsum = wsum * c + e;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    o[dt] = o[dt] * c + e * v[k][dt];
-                m = m_new;
-            }
-        }
-        if (!live[j])
-            continue;
-        const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *(f32x4*)(orow[j] + 16 * dt + 4 * q4) = o[dt] * inv;
-        if (lrow[j] && q4 == 0)
-            *lrow[j] = wsum > 0.f ? m + __logf(wsum) : -__builtin_inff();
-    }
-    reset_counter(counter);
-}
-
-// Rows of an empty sequence (decode step): out = 0, lse = -inf; wave w of
-// the work-group writes query heads w, w + HG, ...
-template <int D>
-__device__ __forceinline__ void write_empty_rows(const DecodeArgs& a, int b, int wave, int HG)
-{
-    for (int hq = wave; hq < a.Hq; hq += HG) {
-        float* o = a.out + ((size_t)b * a.Hq + hq) * D;
-        for (int d = __lane_id(); d < D; d += kWave)
-            o[d] = 0.f;
-        if (a.lse_out && __lane_id() == 0)
-            a.lse_out[(size_t)b * a.Hq + hq] = -__builtin_inff();
-    }
-}
-
 template <int D, int BS, int KVF, int NT, int NCT, bool MQ>
 __global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
@@ -1052,30 +856,16 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const int G = a.G;
     constexpr int kCols = 16 * NCT;                  // MQ columns per wave
     const int cpw = MQ ? kCols : G;                  // workspace rows per wave
-    // tiles of the whole call; a decode step's empty sequences get their
-    // rows here (sequence b from work-group b mod launched groups)
-    long long seq_tiles_all = 0;
-    for (int c = 0; c < a.B; c += kWave) {
-        const int b = c + __lane_id();
-        const int T = b < a.B ? a.context_lens[b] : 1;
-        seq_tiles_all += wave_sum_w<MQ>(b < a.B ? (long long)tiles_of(T) *
-                                                      col_groups<MQ, NCT>(a, b) : 0);
-        if (!MQ) {
-            unsigned long long empty =
-                __ballot(b < a.B && T <= 0 && b % ws.ngroups_launched == wg);
-            while (empty) {
-                const int l = __builtin_ctzll(empty);
-                empty &= empty - 1;
-                write_empty_rows<D>(a, c + l, wave, HG);
-            }
-        }
-    }
-    const long long total = seq_tiles_all * ngroups;
+    const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
     const long long R = ranges_of(ws.ngroups_launched / NS, total);
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
-    if (r >= R || r0 >= r1)
+    CutRecord cut = {0, total, 0, -1, 0, 0, 0, 0, 0};
+    if (r >= R || r0 >= r1) {
+        if (threadIdx.x == 0)
+            ws.cuts[wg] = cut;
         return;
+    }
     int b;
     long long before;
     locate_tile<MQ, NCT>(a, ngroups, r0, b, before);
@@ -1083,45 +873,10 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     int n = tiles_of(T);
     int ncg = col_groups<MQ, NCT>(a, b);
     int u = (int)((r0 - before * ngroups) / n);      // unit of b: hg * ncg + cg
-    constexpr int TPS = balanced_tps<KVF, MQ>();
-    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, KVF, NCT, TPS>();
-
-    // the output rows of this wave's columns of (sequence b, kv head h,
-    // column group cg)
-    auto columns = [&](int bb, int h, int cg, bool (&live)[NCT], float* (&orow)[NCT],
-                       float* (&lrow)[NCT]) {
-        if (!MQ) {
-            const int hq = h * G + r16;
-            live[0] = r16 < G;
-            const size_t row = (size_t)bb * a.Hq + (live[0] ? hq : 0);
-            orow[0] = a.out + row * D;
-            lrow[0] = a.lse_out ? a.lse_out + row : nullptr;
-            return;
-        }
-        const int qs = a.query_start[bb];
-        const int q = a.query_start[bb + 1] - qs;
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-            const int c = cg * kCols + 16 * j + r16;
-            const int i = c / G;
-            live[j] = i < q;
-            const size_t row = (size_t)(qs + (live[j] ? i : 0)) * a.Hq + h * G + (c - i * G);
-            orow[j] = a.out + row * D;
-            lrow[j] = a.lse_out ? a.lse_out + row : nullptr;
-        }
-    };
-
-    // Cut pieces are stored as they finish; their arrivals (and a merge when
-    // this wave's piece is a unit's last to arrive) wait until the whole
-    // range is streamed, so no wave stalls on a counter mid-range.  A range
-    // holds at most two cut pieces: its first and its last.
-    struct Pending {
-        CutUnit cu;
-        int b, h, cg;
-    };
-    Pending pend0, pend1;
-    int npend = 0;
+    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, KVF, NCT>();
+    const int rows_per_slot = HG * cpw;
     long long x = r0;
+    int piece = 0;
     while (true) {
         const long long ustart = before * ngroups + (long long)u * n;
         const long long uend = ustart + n;
@@ -1133,67 +888,81 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         const int hg = hl * NS + hs;
         const int h = hg * HG + wave;
         const bool whole = x == ustart && pend == uend;
-        RangeAcc<D> acc[NCT];
+        const size_t slot = 2 * (size_t)wg + (piece == 0 ? 0 : 1);
         if (!MQ) {
-            attend_range<D, BS, KVF, NT, 1, false, TPS>(a, lds, b, h, t_begin, t_end,
-                                                   decode_cols(a, b, h, D),
-                                                   *(RangeAcc<D>(*)[1])acc,
+            RangeAcc<D> acc[1];
+            attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
+                                                   decode_cols(a, b, h, D), acc,
                                                    a.k_new != nullptr && pend == uend);
+            float inv, lse;
+            finish_range<D>(acc[0], inv, lse);
+            if (r16 < G) {
+                const int hq = h * G + r16;
+                if (whole) {
+                    store_row<D>(a.out + ((size_t)b * a.Hq + hq) * D, acc[0], inv);
+                    if (a.lse_out && q4 == 0)
+                        a.lse_out[(size_t)b * a.Hq + hq] = lse;
+                } else {
+                    const size_t row = slot * rows_per_slot + wave * G + r16;
+                    store_row<D>(ws.part_out + row * D, acc[0], inv);
+                    if (q4 == 0)
+                        ws.part_lse[row] = lse;
+                }
+            }
         } else {
             const int qs = a.query_start[b];
             const int q = a.query_start[b + 1] - qs;
             Cols<NCT> cs;
+            int qrow[NCT], hq[NCT];
 #pragma unroll
             for (int j = 0; j < NCT; ++j) {
                 const int c = cg * kCols + 16 * j + r16;
                 const int i = c / G;
                 cs.live[j] = i < q;
-                cs.qrow[j] = a.query
-                             + ((size_t)(qs + (cs.live[j] ? i : 0)) * a.Hq + h * G + (c - i * G))
-                                   * D;
+                qrow[j] = qs + (cs.live[j] ? i : 0);
+                hq[j] = h * G + (c - i * G);
+                cs.qrow[j] = a.query + ((size_t)qrow[j] * a.Hq + hq[j]) * D;
                 cs.lim[j] = T - q + i + 1;
             }
             cs.mask_from = T - q + (cg * kCols) / G + 1;
+            RangeAcc<D> acc[NCT];
             attend_range<D, BS, KVF, NT, NCT, true>(a, lds, b, h, t_begin, t_end, cs, acc);
-        }
-        bool live[NCT];
-        float* orow[NCT];
-        float* lrow[NCT];
-        columns(b, h, cg, live, orow, lrow);
-        if (whole) {
 #pragma unroll
             for (int j = 0; j < NCT; ++j) {
                 float inv, lse;
                 finish_range<D>(acc[j], inv, lse);
-                if (!live[j])
+                if (!cs.live[j])
                     continue;
-                store_row<D>(orow[j], acc[j], inv);
-                if (lrow[j] && q4 == 0)
-                    *lrow[j] = lse;
+                if (whole) {
+                    const size_t orow = (size_t)qrow[j] * a.Hq + hq[j];
+                    store_row<D>(a.out + orow * D, acc[j], inv);
+                    if (a.lse_out && q4 == 0)
+                        a.lse_out[orow] = lse;
+                } else {
+                    const size_t row = slot * rows_per_slot + wave * kCols + 16 * j + r16;
+                    store_row<D>(ws.part_out + row * D, acc[j], inv);
+                    if (q4 == 0)
+                        ws.part_lse[row] = lse;
+                }
             }
-        } else {
-            Pending pd;
-            pd.cu.ustart = ustart;
-            pd.cu.total = total;
-            pd.cu.R = R;
-            pd.cu.rf = range_of(ustart, total, R);
-            pd.cu.rl = range_of(uend - 1, total, R);
-            pd.cu.NS = NS;
-            pd.cu.hs = hs;
-            pd.cu.rows_per_slot = HG * cpw;
-            pd.b = b;
-            pd.h = h;
-            pd.cg = cg;
-            store_cut_piece<D, NCT>(ws, pd.cu, r, wave * cpw, acc, live);
-            if (npend == 0)
-                pend0 = pd;
-            else
-                pend1 = pd;
-            ++npend;
         }
+        ++piece;
         x = pend;
-        if (x >= r1)
+        if (x >= r1) {
+            if (pend < uend && ustart >= r0) {   // this group holds the unit's first piece
+                cut.b = b;
+                cut.u = u;
+                cut.ustart = ustart;
+                cut.n = n;
+                cut.ncg = ncg;
+                cut.rl = range_of(uend - 1, total, R);
+                if (MQ) {
+                    cut.qs = a.query_start[b];
+                    cut.q = a.query_start[b + 1] - cut.qs;
+                }
+            }
             break;
+        }
         if (++u == ngroups * ncg) {     // next sequence with a non-empty unit
             u = 0;
             before += (long long)n * ncg;
@@ -1205,15 +974,151 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
             } while (n == 0 || ncg == 0);
         }
     }
-    for (int k = 0; k < npend; ++k) {
-        const Pending& pd = k == 0 ? pend0 : pend1;
-        bool live[NCT];
-        float* orow[NCT];
-        float* lrow[NCT];
-        columns(pd.b, pd.h, pd.cg, live, orow, lrow);
-        int* counter = ws.counters + (pd.cu.rf * NS + hs) * HG + wave;
-        arrive_and_merge<D, NCT>(ws, pd.cu, counter, wave * cpw, live, orow, lrow);
+    if (threadIdx.x == 0)
+        ws.cuts[wg] = cut;
+}
+
+// Merge of the recorded cut units.  Work-group (r, y) takes the unit that
+// work-group r of the main launch recorded and merges kMergeWaves of its
+// rows, one wave per row (row = kv head of the group x column).  Lane
+// (p, c) owns four output elements (column c) and every npg-th piece
+// starting at p; the npg partial sums meet through lane butterflies.
+// The extra column r = R writes out = 0, lse = -inf for the rows of empty
+// sequences (decode step only: with several new tokens an empty sequence
+// has no rows).
+constexpr int kMergeWaves = 4;
+
+template <int D, int NCT, bool MQ>
+__global__ __launch_bounds__(kMergeWaves * kWave)
+void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
+{
+    constexpr int cols = D / 4;
+    constexpr int npg = kWave / cols;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int HG = ws.head_group;
+    const int G = a.G;
+    constexpr int kCols = 16 * NCT;
+    const int cpw = MQ ? kCols : G;
+    if ((long long)blockIdx.x == ws.ngroups_launched) {
+        if (MQ)
+            return;
+        for (int b = blockIdx.y; b < a.B; b += gridDim.y) {
+            if (a.context_lens[b] > 0)
+                continue;
+            for (int hq = wave; hq < a.Hq; hq += kMergeWaves) {
+                float* o = a.out + ((size_t)b * a.Hq + hq) * D;
+                for (int d = lane; d < D; d += kWave)
+                    o[d] = 0.f;
+                if (a.lse_out && lane == 0)
+                    a.lse_out[(size_t)b * a.Hq + hq] = -__builtin_inff();
+            }
+        }
+        return;
     }
+    const CutRecord rec = ws.cuts[blockIdx.x];
+    const int b = rec.b;
+    if (b < 0)
+        return;
+    const int in_slot = blockIdx.y * kMergeWaves + wave;   // w * cpw + column
+    if (in_slot >= HG * cpw)
+        return;
+    const int NS = ws.head_split;
+    const int hs = (int)(blockIdx.x % NS);           // record of work-group blockIdx.x
+    const int u = rec.u;
+    const int hl = MQ ? u / rec.ncg : u;
+    const int cg = MQ ? u - hl * rec.ncg : 0;
+    const int h = (hl * NS + hs) * HG + in_slot / cpw;
+    const int cc = in_slot % cpw;
+    size_t orow;
+    if (!MQ) {
+        if (cc >= G)
+            return;
+        orow = (size_t)b * a.Hq + h * G + cc;
+    } else {
+        const int col = cg * kCols + cc;
+        const int i = col / G;
+        if (i >= rec.q)
+            return;
+        orow = (size_t)(rec.qs + i) * a.Hq + h * G + (col - i * G);
+    }
+    float* o = a.out + orow * D;
+    const long long total = rec.total;
+    const long long R = ranges_of(ws.ngroups_launched / NS, total);
+    const long long ustart = rec.ustart;
+    const long long rf = blockIdx.x / NS;             // range holding the first piece
+    const long long rl = rec.rl;
+    const int rows_per_slot = HG * cpw;
+    // Groups between rf and rl with an empty range (fewer tiles than
+    // groups) hold no piece of this unit.
+    auto piece_row = [&](long long r) -> long long {
+        const long long s0 = range_start(r, total, R);
+        if (range_start(r + 1, total, R) <= s0)
+            return -1;
+        const long long slot = 2 * (r * NS + hs) + ((r == rf && s0 < ustart) ? 1 : 0);
+        return slot * rows_per_slot + in_slot;
+    };
+    const int p0 = lane / cols;
+    const int c4 = lane % cols;
+    // one online pass (running max, rescaled sums) over this lane's
+    // pieces, eight pieces' loads in flight per step
+    constexpr int kBatch = 8;
+    float m = -__builtin_inff();
+    float wsum = 0.f;
+    f32x4 accv = {0.f, 0.f, 0.f, 0.f};
+    for (long long base = rf + p0; base <= rl; base += kBatch * npg) {
+        long long pr[kBatch];
+        float l[kBatch];
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const long long r = base + (long long)k * npg;
+            pr[k] = r <= rl ? piece_row(r) : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            l[k] = -__builtin_inff();
+            v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (pr[k] >= 0) {
+                l[k] = ws.part_lse[pr[k]];
+                v[k] = *(const f32x4*)(ws.part_out + pr[k] * D + 4 * c4);
+            }
+        }
+        float mb = l[0];
+#pragma unroll
+        for (int k = 1; k < kBatch; ++k)
+            mb = fmaxf(mb, l[k]);
+        const float m_new = fmaxf(m, mb);
+        if (m_new == -__builtin_inff())
+            continue;
+        const float sc = __expf(m - m_new);
+        wsum *= sc;
+        accv *= sc;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const float wt = __expf(l[k] - m_new);
+            wsum += wt;
+            accv += wt * v[k];
+        }
+        m = m_new;
+    }
+    // bring the npg lane groups of a column to a common max, then add them
+    const float mrow = wave_max(m);
+    const float f = __expf(m - mrow);
+    wsum *= f;
+    accv *= f;
+    m = mrow;
+#pragma unroll
+    for (int k = cols; k < kWave; k <<= 1) {
+        wsum += xor_shuffle(wsum, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            accv[e] += xor_shuffle(accv[e], k);
+    }
+    if (lane < cols)
+        *(f32x4*)(o + 4 * c4) = accv * (1.0f / wsum);
+    if (a.lse_out && lane == 0)
+        a.lse_out[orow] = m + __logf(wsum);
 }
 
 template <int D, int BS, int KVF, int NCT, bool MQ>
@@ -1223,8 +1128,7 @@ int balanced_occupancy(int head_group)
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks,
             reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>),
-            head_group * kWave,
-            (size_t)head_group * wave_lds_bytes<D, KVF, NCT, balanced_tps<KVF, MQ>()>())
+            head_group * kWave, (size_t)head_group * wave_lds_bytes<D, KVF, NCT>())
         != hipSuccess)
         return 0;
     return blocks;
@@ -1234,8 +1138,7 @@ template <int D, int BS, int KVF, int NCT, bool MQ>
 hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt,
                              hipStream_t stream)
 {
-    const size_t lds =
-        (size_t)ws.head_group * wave_lds_bytes<D, KVF, NCT, balanced_tps<KVF, MQ>()>();
+    const size_t lds = (size_t)ws.head_group * wave_lds_bytes<D, KVF, NCT>();
     const dim3 grid((unsigned)ws.ngroups_launched), block(ws.head_group * kWave);
     if (nt)
         hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>), grid, block, lds,
@@ -1243,6 +1146,14 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt
     else
         hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 0, NCT, MQ>), grid, block, lds,
                            stream, a, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int cpw = MQ ? 16 * NCT : a.G;
+    const unsigned ychunks = (unsigned)((ws.head_group * cpw + kMergeWaves - 1) / kMergeWaves);
+    const dim3 mgrid((unsigned)ws.ngroups_launched + 1, ychunks);
+    hipLaunchKernelGGL((balanced_merge_kernel<D, NCT, MQ>), mgrid, dim3(kMergeWaves * kWave), 0,
+                       stream, a, ws);
     return hipGetLastError();
 }
 

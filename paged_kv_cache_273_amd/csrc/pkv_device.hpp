@@ -87,66 +87,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
-// Exchange between work-groups of one launch.  The L2 caches are per XCD,
-// so a plain store of one work-group may sit in an L2 that another
-// work-group does not read.  Agent-scope relaxed atomic stores and loads
-// are device-coherent by themselves (the compiler's memory model for
-// gfx950 gives them the sc1 cache policy: written through to, and read
-// from, the device's coherence point), so data exchanged only through
-// them needs no L2 write-back or invalidate: after the writer's stores
-// have completed (s_waitcnt vmcnt(0)), an atomic counter update orders
-// them before any reader that sees the update.  8-byte pieces.
-__device__ __forceinline__ void store_coherent(float* p, f32x4 v)
-{
-    const u32x4 u = __builtin_bit_cast(u32x4, v);
-    unsigned long long* q = (unsigned long long*)p;
-    __hip_atomic_store(q, (unsigned long long)u[0] | ((unsigned long long)u[1] << 32),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, (unsigned long long)u[2] | ((unsigned long long)u[3] << 32),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ f32x4 load_coherent(const float* p)
-{
-    unsigned long long* q = (unsigned long long*)p;
-    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long b =
-        __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_bit_cast(f32x4, u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b,
-                                            (uint32_t)(b >> 32)});
-}
-
-__device__ __forceinline__ void store_coherent_f32(float* p, float v)
-{
-    __hip_atomic_store((uint32_t*)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float load_coherent_f32(const float* p)
-{
-    return __builtin_bit_cast(
-        float, __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
-// Counts the calling wave in an arrival counter once every device-coherent
-// store it issued before has completed; returns the count before it (the
-// same value in every lane).  The wait also drains loads in flight, so
-// call it where none are.
-__device__ __forceinline__ int arrive(int* counter)
-{
-    __builtin_amdgcn_s_waitcnt(0);
-    int old = 0;
-    if (__lane_id() == 0)
-        old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_amdgcn_readlane(old, 0);
-}
-
-__device__ __forceinline__ void reset_counter(int* counter)
-{
-    if (__lane_id() == 0)
-        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Butterfly exchange across lanes (lane ^ mask) through ds_bpermute.
 __device__ __forceinline__ float xor_shuffle(float v, int mask)
 {

@@ -49,17 +49,26 @@ struct DecodeArgs {
     const uint16_t* v_new = nullptr;
 };
 
-// Workspace of the balanced schedule: one arrival counter per (launched
-// work-group, kv head of the group) in the first kCounterBytes (zero
-// before a call, left zero by it), then 2 partial slots per launched
-// work-group, each with head_group * C rows (C = G for a decode step,
-// 16 * column tiles with several new tokens) of D floats, then as many lse.
-constexpr long long kCounterBytes = 64 * 1024;
+// The unit a work-group starts but leaves unfinished (b < 0: none), with
+// everything its merge needs.
+struct CutRecord {
+    long long ustart;         // linear index of the unit's first tile
+    long long total;          // tiles of the whole call
+    long long rl;             // range holding the unit's last tile
+    int32_t b, u;             // sequence, unit of the sequence in the tile list (head
+                              // group of the list, column group)
+    int32_t n, ncg;           // tiles of the unit, column groups of the sequence
+    int32_t qs, q;            // several new tokens: first row and rows of the sequence
+};
 
+// Workspace of the balanced schedule: 2 partial slots per launched
+// work-group, each with head_group * C rows (C = G for a decode step,
+// 16 * column tiles with several new tokens) of D floats and as many lse,
+// then one CutRecord per work-group.
 struct BalanceArgs {
-    int* counters;            // [ngroups_launched * head_group]
     float* part_out;          // [2 * ngroups_launched, head_group * C, D]
     float* part_lse;          // [2 * ngroups_launched, head_group * C]
+    CutRecord* cuts;          // [ngroups_launched], 16-byte aligned
     int32_t ngroups_launched; // work-groups of the decode launch (a multiple of head_split)
     int32_t head_group;       // kv heads per work-group (divides Hkv, <= 8)
     int32_t head_split;       // work-groups sharing each token range (their head groups

@@ -95,8 +95,7 @@ def test_tiny_step(orc, pkv, kind, mode):
         out = pkv.split_context_reduce(po, pl, d.cl, 48, lse_out=lse)
     else:
         ws = pkv.make_workspace(d.q, d.k, kv_dtype=d.dt)
-        ws.fill_(0xFF)                          # scratch garbage; counters zero
-        ws[:pkv.WORKSPACE_COUNTER_BYTES].zero_()
+        ws.fill_(0xFF)
         out = pkv.paged_decode_attention_balanced(d.q, d.k, d.v, d.bt, d.cl, sc, workspace=ws,
                                                   lse_out=lse, **kw)
     torch.cuda.synchronize()

@@ -99,8 +99,7 @@ def _fused(pkv, inp, d, mode, split=48):
         out = pkv.split_context_reduce(po, pl, d.cl, split, lse_out=lse)
     else:
         ws = pkv.make_workspace(d.q, d.k, kv_dtype=d.kw["kv_dtype"])
-        ws.fill_(0xFF)                          # scratch garbage; counters zero
-        ws[:pkv.WORKSPACE_COUNTER_BYTES].zero_()
+        ws.fill_(0xFF)
         out = pkv.paged_append_decode_attention_balanced(d.q, d.k_new, d.v_new, d.k, d.v, d.bt,
                                                          d.cl, sc, workspace=ws, lse_out=lse,
                                                          **d.kw)
