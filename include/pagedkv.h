@@ -297,6 +297,32 @@ int paged_append_decode_attention_balanced(const uint16_t* query,
                                            float* out, float* lse_out, void* stream);
 
 /*
+ * paged_decode_attention_balanced_noalloc -- paged_decode_attention_balanced
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results without workspace / workspace_bytes.  Its workspace
+ * is a static device array inside the library, 18 MiB per GPU, held from
+ * the library's first use on that GPU until the process ends (its contents
+ * on entry do not matter, as for a caller-owned workspace).  Nothing is
+ * allocated or freed by any call.  All calls on one GPU share that GPU's
+ * array: calls that may overlap on one GPU (different streams, threads
+ * without ordering) race and give wrong results; order them on one stream.
+ *  Returns PKV_EUNSUPPORTED when the workspace of these shapes on this
+ *  device (paged_decode_workspace_size) exceeds 18 MiB, PKV_ELAUNCH if the
+ *  array's device address cannot be obtained, otherwise as
+ *  paged_decode_attention_balanced.
+ */
+int paged_decode_attention_balanced_noalloc(const uint16_t* query,
+                                            const void* k_cache, const void* v_cache,
+                                            const float* k_scale, const float* v_scale,
+                                            const int32_t* block_tables, int32_t max_blocks,
+                                            const int32_t* context_lens,
+                                            int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t block_size, int32_t num_blocks,
+                                            int32_t kv_dtype, float scale,
+                                            float* out, float* lse_out, void* stream);
+
+/*
  * Bytes of workspace paged_decode_attention_balanced needs for these
  * head counts and cache format on the current device (it depends on the
  * device's compute-unit count), or a negative pkv_status.  Independent of

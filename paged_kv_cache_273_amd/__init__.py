@@ -37,7 +37,7 @@ EXPORTS = ("paged_kv_append", "paged_decode_attention", "split_context_reduce",
            "paged_append_decode_attention", "paged_append_decode_attention_balanced",
            "paged_kv_write", "paged_multiquery_attention", "paged_multiquery_workspace_size",
            "pkv_status_string", "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
-           "paged_kv_copy_blocks",
+           "paged_kv_copy_blocks", "paged_decode_attention_balanced_noalloc",
            # host block manager (include/pkv_block_manager.h; binding in block_manager.py)
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add", "pkv_bm_append",
            "pkv_bm_append_batch", "pkv_bm_fork",
@@ -72,6 +72,9 @@ def _load(path=LIB_PATH):
     L.paged_decode_attention_balanced.restype = C.c_int
     L.paged_decode_attention_balanced.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I,
                                                   C.c_float, P, C.c_int64, P, P, P]
+    L.paged_decode_attention_balanced_noalloc.restype = C.c_int
+    L.paged_decode_attention_balanced_noalloc.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I,
+                                                          I, I, I, C.c_float, P, P, P]
     L.paged_append_decode_attention_balanced.restype = C.c_int
     L.paged_append_decode_attention_balanced.argtypes = (
         [P, P, P] + L.paged_decode_attention_balanced.argtypes[1:])
@@ -359,6 +362,31 @@ def paged_append_decode_attention_balanced(query, k_new, v_new, k_cache, v_cache
     return _balanced("paged_append_decode_attention_balanced", query, (k_new, v_new), k_cache,
                      v_cache, block_tables, context_lens, scale, workspace, out, lse_out,
                      k_scale, v_scale, kv_dtype, stream)
+
+
+def paged_decode_attention_balanced_noalloc(query, k_cache, v_cache, block_tables,
+                                            context_lens, scale, *, out, lse_out=None,
+                                            k_scale=None, v_scale=None, kv_dtype=None,
+                                            stream=None):
+    """paged_decode_attention_balanced without a workspace argument: the
+    library's static per-GPU scratch array serves as the workspace, so the
+    call allocates nothing (for callers that cannot allocate).  `out` must
+    be given.  Calls that may overlap on one GPU race."""
+    nb, bs, Hkv, D, code = _cache_args(k_cache, v_cache, k_scale, v_scale, kv_dtype)
+    _shape(query, (None, None, D), "query", _BF16_BITS)
+    B, Hq = int(query.shape[0]), int(query.shape[1])
+    max_blocks = _table_args(block_tables, context_lens, B)
+    _shape(out, (B, Hq, D), "out", (torch.float32,))
+    if lse_out is not None:
+        _shape(lse_out, (B, Hq), "lse_out", (torch.float32,))
+    _same_device(k_cache, query=query, block_tables=block_tables, context_lens=context_lens,
+                 out=out, lse_out=lse_out)
+    st = _lib.paged_decode_attention_balanced_noalloc(
+        _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), max_blocks, _ptr(context_lens), B, Hq, Hkv, D, bs, nb, code,
+        float(scale), _ptr(out), _ptr(lse_out), _stream(stream))
+    _check("paged_decode_attention_balanced_noalloc", st)
+    return out
 
 
 def split_context_reduce(partial_out, partial_lse, context_lens, split_tokens, *, out=None,

@@ -93,6 +93,40 @@ bool stream_kv_loads(int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_
 
 } // namespace
 
+// ------------------------------------------------------------- no allocation
+// The allocation-free form of paged_decode_attention_balanced keeps its
+// workspace in this file-scope device array (one copy per GPU, held until
+// the process ends).  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): the device address of
+// each GPU's copy comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr int64_t kStaticScratchBytes = (int64_t)18 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's scratch array, or null on failure.
+void* device_scratch()
+{
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    if (addr[dev])
+        return addr[dev];
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return nullptr;
+    addr[dev] = p;
+    return p;
+}
+
+} // namespace
+
 extern "C" {
 
 const char* pkv_status_string(int status)
@@ -432,6 +466,34 @@ int paged_decode_attention_balanced(const uint16_t* query, const void* k_cache,
     return balanced_call(query, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
                          block_tables, max_blocks, context_lens, B, Hq, Hkv, D, block_size,
                          num_blocks, kv_dtype, scale, workspace, workspace_bytes, out, lse_out,
+                         stream);
+}
+
+int paged_decode_attention_balanced_noalloc(const uint16_t* query, const void* k_cache,
+                                            const void* v_cache, const float* k_scale,
+                                            const float* v_scale, const int32_t* block_tables,
+                                            int32_t max_blocks, const int32_t* context_lens,
+                                            int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t block_size, int32_t num_blocks,
+                                            int32_t kv_dtype, float scale, float* out,
+                                            float* lse_out, void* stream)
+{
+    // the workspace this call needs must fit the static array
+    const int64_t need = paged_decode_workspace_size(Hq, Hkv, D, block_size, kv_dtype);
+    if (need < 0)
+        return (int)need;
+    if (need > kStaticScratchBytes)
+        return PKV_EUNSUPPORTED;
+    if (B == 0)
+        return balanced_call(query, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                             block_tables, max_blocks, context_lens, B, Hq, Hkv, D, block_size,
+                             num_blocks, kv_dtype, scale, nullptr, 0, out, lse_out, stream);
+    void* ws = device_scratch();
+    if (!ws)
+        return PKV_ELAUNCH;
+    return balanced_call(query, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                         block_tables, max_blocks, context_lens, B, Hq, Hkv, D, block_size,
+                         num_blocks, kv_dtype, scale, ws, kStaticScratchBytes, out, lse_out,
                          stream);
 }
 

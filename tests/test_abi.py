@@ -69,7 +69,8 @@ def test_header_declares_the_boundary():
                             "paged_kv_gather_blocks", "paged_kv_scatter_blocks",
                             "paged_kv_copy_blocks", "pkv_status_string",
                             "paged_append_decode_attention",
-                            "paged_append_decode_attention_balanced"]), names
+                            "paged_append_decode_attention_balanced",
+                            "paged_decode_attention_balanced_noalloc"]), names
 
 
 def test_block_manager_header_declares_its_calls():
