@@ -26,12 +26,13 @@
 //     in its own LDS slice, converting fp8 codes to bf16 on the way;
 //   * S^T[token][head] = K . Q^T on the 16x16x32 bf16 MFMA: the G query
 //     heads of the group (padded to 16 columns) share every K load;
-//   * online softmax over the tile in fp32 (exp2 domain), the max taken
-//     across the wave with two lane butterflies;
-//   * O^T[d][head] += V^T . P^T on the MFMA, V^T read from LDS with a
-//     transposing 16-bit gather (row pitch padded by 8 bytes so the four
-//     lane groups hit disjoint banks); P enters as a hi + lo pair of bf16
-//     terms so the probabilities keep ~16 significant bits.
+//   * online softmax over the tile in fp32 (exp2 domain) against a
+//     reference max that may trail the running max by up to 8 (so the
+//     accumulators are rescaled only on the few tiles that raise it more);
+//   * O^T[d][head] += V^T . P^T on the MFMA, V^T read from LDS with the
+//     transposing 16-bit read of gfx950 (row pitch 2D + 32 bytes so eight
+//     consecutive rows fall on disjoint banks); P enters as a hi + lo pair
+//     of bf16 terms so the probabilities keep ~16 significant bits.
 // The next tile's K/V loads are issued while the current tile is being
 // processed (into the registers the current tile has just released), so
 // every wave keeps up to 16 KB in flight with a single register set.
@@ -68,6 +69,9 @@ constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 #define PKV_MIN_WAVES_PER_EU 2
 #endif
 constexpr int kTile = 32;
+// Largest lag (log2 units) of a column's reference max behind its running
+// max: probabilities stay <= 2^8, far from fp32 / bf16 overflow.
+constexpr float kMaxLag = 8.f;
 // SIMDs of an MI355X (256 CUs x 4): the split decode gives each wave two
 // consecutive splits when that still leaves one wave per SIMD (measured:
 // 1024 longer streams beat 2048 shorter ones by ~2% at 512-token splits)
@@ -99,7 +103,10 @@ struct Cfg {
     static constexpr int V_RPI = kWave / V_LPR;         // V rows per load instruction
     static constexpr int V_LOADS = kTile / V_RPI;       // V loads per tile
     static constexpr int DT = D / 16;                   // 16-wide d tiles of the output
-    static constexpr int PITCH = D * 2 + 8;             // LDS row pitch (bf16 rows), bytes
+    // LDS row pitch of the staged bf16 V rows, bytes: 2D + 32 puts the rows
+    // of 8 consecutive tokens on disjoint 8-dword bank ranges (64 banks), so
+    // the transposing reads of the PV operands are free of bank conflicts
+    static constexpr int PITCH = D * 2 + 32;
     static constexpr int LDS_BYTES = kTile * PITCH;     // per wave
     static constexpr int Q_BYTES = KSTEPS * kWave * 16;  // Q operands of one column tile
     static_assert(16 % V_RPI == 0, "a V load must stay inside one 16-token block");
@@ -335,6 +342,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                    + 16 * (lane % C::V_LPR);
     }
 
+    // byte offsets of this lane's transposing V^T reads in the staged tile
+    const uint32_t tr_off0 = (uint32_t)pv_token(q4, r16 >> 2) * C::PITCH + 8 * (r16 & 3);
+    const uint32_t tr_off1 = (uint32_t)pv_token(q4, 4 + (r16 >> 2)) * C::PITCH + 8 * (r16 & 3);
+
     // Physical blocks (and fp8 scales) of the tile starting at t0.
     auto tile_addr = [&](int t0) {
         TileAddr ta;
@@ -476,42 +487,58 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
             const int lim = CAUSAL ? min(t_end, cs.lim[j]) : t_end;
+            // Scores enter relative to the column's reference max m (0 while
+            // nothing is visible): s = score * log2(e) - m, one fma each.
+            const float m_ref = r[j].m == -__builtin_inff() ? 0.f : r[j].m;
             float s[8];
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
                 const float f = KVF ? sl2 * (tau ? ta.ksB : ta.ksA) : sl2;
-                const float zq = FOLD ? (tau ? ta.kzB : ta.kzA) * qsum[j] : 0.f;
+                // int8: (acc - zp_k * sum(q)) * f - m
+                const float c = FOLD ? (tau ? ta.kzB : ta.kzA) * qsum[j] * f + m_ref : m_ref;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float x = (FOLD ? sacc[j][tau][i] - zq : sacc[j][tau][i]) * f;
+                    float x = __builtin_fmaf(sacc[j][tau][i], f, -c);
                     if (masked && t0 + 16 * tau + 4 * q4 + i >= lim)
                         x = -__builtin_inff();
                     s[4 * tau + i] = x;
                 }
             }
-            float mt = s[0];
+            float lm = s[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i)
-                mt = fmaxf(mt, s[i]);
-            mt = fmaxf(mt, xor_shuffle(mt, 16));
-            mt = fmaxf(mt, xor_shuffle(mt, 32));
-            const float m_new = fmaxf(r[j].m, mt);
-            // a column with nothing visible yet keeps m = -inf; its
-            // exponentials are then taken against 0 and all vanish
-            const float m_ref = (CAUSAL && m_new == -__builtin_inff()) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(r[j].m - m_ref);
-            r[j].m = m_new;
+                lm = fmaxf(lm, s[i]);
+            // The reference may trail the running max by up to kMaxLag (so
+            // p <= 2^kMaxLag): the sums are rescaled only on a column's
+            // first visible tile or when a tile raises its max by more than
+            // that, which in a long range is a handful of tiles.  The
+            // decision is taken for the whole wave.
+            if (__builtin_amdgcn_ballot_w64(lm > kMaxLag || r[j].m == -__builtin_inff())) {
+                float mt = lm;
+                mt = fmaxf(mt, xor_shuffle(mt, 16));
+                mt = fmaxf(mt, xor_shuffle(mt, 32));
+                const float m_new = fmaxf(r[j].m, m_ref + mt);   // -inf: nothing visible yet
+                const float m_ref_new = m_new == -__builtin_inff() ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(r[j].m - m_ref_new);
+                const float delta = m_ref_new - m_ref;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    s[i] -= delta;
+                r[j].m = m_new;
+                r[j].l *= alpha;
+                r[j].corr *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+                    r[j].acc[dt] *= alpha;
+            }
             float p[8];
             float psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+                p[i] = __builtin_amdgcn_exp2f(s[i]);
                 psum += p[i];
             }
-            r[j].l = r[j].l * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-                r[j].acc[dt] *= alpha;
+            r[j].l += psum;
             if (KVF) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -520,9 +547,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                 }
             }
             if (FOLD)
-                r[j].corr = r[j].corr * alpha
-                            + ta.vzA * ((p[0] + p[1]) + (p[2] + p[3]))
-                            + ta.vzB * ((p[4] + p[5]) + (p[6] + p[7]));
+                r[j].corr += ta.vzA * ((p[0] + p[1]) + (p[2] + p[3]))
+                             + ta.vzB * ((p[4] + p[5]) + (p[6] + p[7]));
             // P as a two-term bf16 split, p = hi + lo (about 16 significant
             // bits): one bf16 term alone loses too much when V terms cancel.
             u32x4 pw, pr;
@@ -536,16 +562,14 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             pb_lo[j] = as_bf16x8(pr);
         }
 
-        const unsigned short* l16 = (const unsigned short*)lds;
+        // V^T operand of d tile dt: lane (q, r) needs V[pv_token(q, i)][16 dt + r],
+        // i = 0..7; two transposing reads, lane (q, 4e + k) naming token
+        // pv_token(q, e) (then pv_token(q, 4 + e)) at head-dim 16 dt + 4k
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-            u32x4 vw;
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                uint32_t lo = l16[(pv_token(q4, i) * C::PITCH) / 2 + 16 * dt + r16];
-                uint32_t hi = l16[(pv_token(q4, i + 1) * C::PITCH) / 2 + 16 * dt + r16];
-                vw[i / 2] = lo | (hi << 16);
-            }
+            const u32x2 x0 = lds_read_tr16(lds + tr_off0 + 32 * dt);
+            const u32x2 x1 = lds_read_tr16(lds + tr_off1 + 32 * dt);
+            const u32x4 vw = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
             for (int j = 0; j < NCT; ++j) {
                 r[j].acc[dt] = mfma_16x16x32(as_bf16x8(vw), pb[j], r[j].acc[dt]);

@@ -82,6 +82,22 @@ __device__ __forceinline__ void u8x16_to_bf16x16(u32x4 codes, float zp, u32x4& l
     hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// Transposing LDS read of 16-bit elements (ds_read_b64_tr_b16, gfx950).
+// Each lane names 8 bytes (4 elements); inside every group of 16 lanes,
+// lane r receives as its element e the element r % 4 of what lane
+// 4e + r / 4 of the group named (layout checked on the device).  So if
+// lane 4e + k names row e of a matrix at column 4k, lane r gets column r
+// of rows 0..3: four rows read across sixteen columns come back as a
+// matrix-core operand holding four rows of one column per lane.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* lds_ptr)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_u8*)lds_ptr);
+    return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
 {
     return __builtin_bit_cast(float, bits16 << 16);
