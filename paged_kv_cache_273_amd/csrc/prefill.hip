@@ -15,11 +15,11 @@
 // the decode-shaped path does) would read the context once per 32 columns.
 // Here a work-group of 8 waves takes 256 columns of one (sequence, kv head)
 // and streams the context once for all of them: each 32-token tile of K and
-// V is loaded by the whole group, converted to bf16 and staged in LDS
-// (double-buffered, one barrier per tile) -- V already transposed, so a
-// lane fetches its 8 PV contraction tokens with two 8-byte reads; every
-// wave then forms its two 16-column score tiles from LDS K, runs the online
-// softmax and accumulates V^T . P^T, as the decode tile body does.
+// V is loaded by the whole group, converted to bf16 and staged in LDS as
+// rows (double-buffered, one barrier per tile); every wave then forms its
+// two 16-column score tiles from LDS K, runs the online softmax and
+// accumulates V^T . P^T, its V^T operands fetched with the transposing
+// LDS read, as the decode tile body does.
 // Work-groups that share a (sequence, kv head) are placed on one XCD so
 // their re-reads of the context hit that XCD's L2.
 //
@@ -38,6 +38,14 @@ constexpr int kPCols = 32;                         // MFMA columns per wave
 constexpr int kPGroupCols = kPWaves * kPCols;      // columns per work-group
 constexpr int kPTile = 32;                         // tokens per staged tile
 constexpr int kXcds = 8;
+// Largest lag (log2 units) of a column's reference max behind its running
+// max: probabilities stay <= 2^8.
+constexpr float kMaxLag = 8.f;
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
 
 template <int D, int KVF>
 struct PCfg {
@@ -47,9 +55,11 @@ struct PCfg {
     static constexpr int NCHUNK = kPTile * CPR;        // chunks per K (or V) tile
     static constexpr int CPT = (2 * NCHUNK + kPThreads - 1) / kPThreads;  // per thread
     static constexpr int KPITCH = D * 2 + 16;          // bf16 K row pitch in LDS
-    static constexpr int VTPITCH = kPTile * 2 + 8;     // bf16 V^T row (one head-dim element)
+    // bf16 V row pitch: eight consecutive rows on disjoint banks for the
+    // transposing reads
+    static constexpr int VPITCH = D * 2 + 32;
     static constexpr int KBYTES = kPTile * KPITCH;
-    static constexpr int BUF = KBYTES + D * VTPITCH;
+    static constexpr int BUF = KBYTES + kPTile * VPITCH;
     static constexpr int KSTEPS = D / 32;
     static constexpr int DT = D / 16;
 };
@@ -169,22 +179,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
             const int rem = c - kv * C::NCHUNK;
             const int row = rem / C::CPR;
             const int col = rem - row * C::CPR;
-            unsigned char* dst = kl + row * C::KPITCH;
-            // V^T: element d of token `row` at vl + d * VTPITCH + 2 * row
-            auto put_vt = [&](int d0, const u32x4& w) {
-                unsigned short* vt = (unsigned short*)(vl + d0 * C::VTPITCH) + row;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    vt[e * (C::VTPITCH / 2)] = (unsigned short)(w[e / 2] >> (16 * (e & 1)));
-            };
+            unsigned char* dst = kv ? vl + row * C::VPITCH : kl + row * C::KPITCH;
             if (!KVF) {
-                if (kv) {
-                    put_vt(8 * col, reg[u]);
-                } else {
-                    u32x2* d2 = (u32x2*)(dst + 16 * col);
-                    d2[0] = u32x2{reg[u][0], reg[u][1]};
-                    d2[1] = u32x2{reg[u][2], reg[u][3]};
-                }
+                u32x2* d2 = (u32x2*)(dst + 16 * col);
+                d2[0] = u32x2{reg[u][0], reg[u][1]};
+                d2[1] = u32x2{reg[u][2], reg[u][3]};
             } else {
                 u32x4 lo, hi;
                 const int t = t0 + row;
@@ -200,16 +199,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
                         hi = u32x4{0u, 0u, 0u, 0u};
                     }
                 }
-                if (kv) {
-                    put_vt(16 * col, lo);
-                    put_vt(16 * col + 8, hi);
-                } else {
-                    u32x2* d2 = (u32x2*)(dst + 32 * col);
-                    d2[0] = u32x2{lo[0], lo[1]};
-                    d2[1] = u32x2{lo[2], lo[3]};
-                    d2[2] = u32x2{hi[0], hi[1]};
-                    d2[3] = u32x2{hi[2], hi[3]};
-                }
+                u32x2* d2 = (u32x2*)(dst + 32 * col);
+                d2[0] = u32x2{lo[0], lo[1]};
+                d2[1] = u32x2{lo[2], lo[3]};
+                d2[2] = u32x2{hi[0], hi[1]};
+                d2[3] = u32x2{hi[2], hi[3]};
             }
         }
     };
@@ -225,10 +219,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
         l_run[j] = 0.f;
     }
     const float sl2 = a.scale_log2;
+    const uint32_t tr_off0 = (uint32_t)(4 * q4 + (r16 >> 2)) * C::VPITCH + 8 * (r16 & 3);
 
-    auto compute = [&](int t0, int buf) {
+    // masked: some column's causal limit falls inside the tile (a
+    // compile-time flag, so unmasked tiles carry no per-score selects)
+    auto compute = [&](int t0, int buf, auto masked_c) {
+        constexpr bool masked = decltype(masked_c)::value;
         const unsigned char* kl = lds + buf * C::BUF;
-        const unsigned char* vt = kl + C::KBYTES;
+        const unsigned char* vl = kl + C::KBYTES;
         float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
         if (KVF) {
 #pragma unroll
@@ -252,45 +250,55 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
                 sacc[1][tau] = mfma_16x16x32(as_bf16x8(kw), qf[1][k], sacc[1][tau]);
             }
         }
-        const bool masked = t0 + kPTile > wave_from;
         bf16x8 pb[2], pb_lo[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+            // scores relative to the column's reference max (0 while nothing
+            // is visible), which may trail the running max by up to kMaxLag
+            const float m_ref = m_run[j] == -__builtin_inff() ? 0.f : m_run[j];
             float s[8];
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
                 const float f = KVF ? sl2 * ks[tau] : sl2;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float x = sacc[j][tau][i] * f;
+                    float x = __builtin_fmaf(sacc[j][tau][i], f, -m_ref);
                     if (masked && t0 + 16 * tau + 4 * q4 + i >= lim[j])
                         x = -__builtin_inff();
                     s[4 * tau + i] = x;
                 }
             }
-            float mt = s[0];
+            float lm = s[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i)
-                mt = fmaxf(mt, s[i]);
-            mt = fmaxf(mt, xor_shuffle(mt, 16));
-            mt = fmaxf(mt, xor_shuffle(mt, 32));
-            const float m_new = fmaxf(m_run[j], mt);
-            const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
-            m_run[j] = m_new;
-            float p[8];
-            float psum = 0.f;
+                lm = fmaxf(lm, s[i]);
+            // rescale only on a column's first visible tile or when a tile
+            // raises its max by more than kMaxLag (decided for the wave)
+            if (__builtin_amdgcn_ballot_w64(lm > kMaxLag || m_run[j] == -__builtin_inff())) {
+                float mt = lm;
+                mt = fmaxf(mt, xor_shuffle(mt, 16));
+                mt = fmaxf(mt, xor_shuffle(mt, 32));
+                const float m_new = fmaxf(m_run[j], m_ref + mt);
+                const float m_ref_new = m_new == -__builtin_inff() ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref_new);
+                const float delta = m_ref_new - m_ref;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
-                psum += p[i];
-            }
-            l_run[j] = l_run[j] * alpha + psum;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {     // a running max moved
+                for (int i = 0; i < 8; ++i)
+                    s[i] -= delta;
+                m_run[j] = m_new;
+                l_run[j] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt)
                     acc[j][dt] *= alpha;
             }
+            float p[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(s[i]);
+                psum += p[i];
+            }
+            l_run[j] += psum;
             if (KVF) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -311,10 +319,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-            // contraction slots (q4, 0..3) = tokens 4q4.., (q4, 4..7) = 16 + 4q4..
-            const unsigned char* row = vt + (16 * dt + r16) * C::VTPITCH;
-            const u32x2 a0 = *(const u32x2*)(row + 8 * q4);
-            const u32x2 a1 = *(const u32x2*)(row + 32 + 8 * q4);
+            // contraction slots (q4, 0..3) = tokens 4q4.., (q4, 4..7) = 16 + 4q4..:
+            // lane (q4, 4e + k) names token 4q4 + e (then 16 + 4q4 + e) at
+            // head-dim 16 dt + 4k, and receives column 16 dt + r16 of the four
+            const u32x2 a0 = lds_read_tr16(vl + tr_off0 + 32 * dt);
+            const u32x2 a1 = lds_read_tr16(vl + tr_off0 + 16 * C::VPITCH + 32 * dt);
             const u32x4 vw = {a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -327,20 +336,29 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(DecodeArgs a, int32_
     // pipeline: the next tile's loads are in flight while this one is
     // computed; one barrier per tile hands the buffers over
     const int ntiles = (t_end + kPTile - 1) / kPTile;
-    fetch(0);
-    stage(0, 0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
+    // tiles below every causal limit of the group (wave 0 holds its lowest
+    // rows): no masking; the loop bounds are uniform over the group, so
+    // every wave meets every barrier
+    const int group_from = T - q + (rb * kPGroupCols) / G + 1;
+    const int n_plain = min(ntiles, group_from / kPTile);
+    auto iteration = [&](int it, auto masked_c) {
         const int t0 = it * kPTile;
         const bool more = it + 1 < ntiles;
         if (more)
             fetch(t0 + kPTile);
         if (t0 < wave_end)
-            compute(t0, it & 1);
+            compute(t0, it & 1, masked_c);
         if (more)
             stage(t0 + kPTile, (it + 1) & 1);
         __syncthreads();
-    }
+    };
+    fetch(0);
+    stage(0, 0);
+    __syncthreads();
+    for (int it = 0; it < n_plain; ++it)
+        iteration(it, Flag<false>());
+    for (int it = n_plain; it < ntiles; ++it)
+        iteration(it, Flag<true>());
 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
