@@ -671,8 +671,10 @@ int paged_multiquery_attention(const uint16_t* query, const int32_t* query_start
     a.sc_head = fmt.sc_head;
     pkv::BalanceArgs ws;
     ws.head_group = pkv::balanced_head_group(Hkv, nct, fmt.kvf);
-    ws.head_split = 1;
-    ws.ngroups_launched = n;
+    // as for a decode step: the Hkv / 4 four-head groups of a token range
+    // run side by side
+    ws.head_split = pkv::balanced_one_group_per_cu(Hkv, nct, fmt.kvf) ? Hkv / ws.head_group : 1;
+    ws.ngroups_launched = n / ws.head_split * ws.head_split;
     carve_workspace(ws, workspace, (int64_t)ws.head_group * 16 * nct, D);
     // range boundaries in double precision: (tiles of the call) * (groups
     // launched) must stay below 2^52

@@ -762,6 +762,7 @@ void decode_kernel(DecodeArgs a)
 // may not see.
 
 constexpr int kMaxHeadGroup = 8;
+constexpr int kMaxMqHeadGroup = 4;
 
 __device__ __forceinline__ int tiles_of(int T)
 {
@@ -859,8 +860,13 @@ __device__ __forceinline__ long long range_of(long long x, long long total, long
     return r;
 }
 
+// Several new tokens over a bf16 cache: at most four-wave groups at one
+// wave per SIMD, so a wave may hold 512 registers (its column tiles'
+// accumulators, the tile in flight and the softmax state spilled to
+// scratch within 256).
 template <int D, int BS, int KVF, int NT, int NCT, bool MQ>
-__global__ __launch_bounds__(kMaxHeadGroup * kWave, PKV_MIN_WAVES_PER_EU)
+__global__ __launch_bounds__((MQ && KVF == 0) ? kMaxMqHeadGroup * kWave : kMaxHeadGroup * kWave,
+                             (MQ && KVF == 0) ? 1 : PKV_MIN_WAVES_PER_EU)
 void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_all[];  // HG slices
@@ -1220,15 +1226,21 @@ bool balanced_one_group_per_cu(int Hkv, int nct, int kvf)
     // streams; measured 4-14% faster than eight-head groups at two per CU
     // (bf16: 70B ragged, 8B, 32k; fp8: 8B and the 36-layer calls; equal
     // on the 70B fp8 batch).  int8 keeps a second wave per SIMD to hide its
-    // heavier conversion (9% slower with one on the 70B batch).
-    return nct == 0 && kvf != 2 && Hkv % 4 == 0;
+    // heavier conversion (9% slower with one on the 70B batch).  Several
+    // new tokens over a bf16 cache: four-head groups, one per CU (the
+    // kernel's launch bounds give such waves 512 registers; 4-token
+    // verification of the 70B batch +15%); the 1-byte formats keep two
+    // waves per SIMD (fp8 -6%, int8 -12% with one).
+    if (nct > 0)
+        return kvf == 0 && Hkv % 4 == 0;
+    return kvf != 2 && Hkv % 4 == 0;
 }
 
 int balanced_head_group(int Hkv, int nct, int kvf)
 {
     if (balanced_one_group_per_cu(Hkv, nct, kvf))
         return 4;
-    for (int hg = kMaxHeadGroup; hg > 1; --hg)
+    for (int hg = (nct > 0 && kvf == 0) ? kMaxMqHeadGroup : kMaxHeadGroup; hg > 1; --hg)
         if (Hkv % hg == 0)
             return hg;
     return 1;
