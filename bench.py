@@ -682,18 +682,21 @@ def _bench_block_manager(a):
 def _measured_traffic(path, key):
     """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes recorded in profiles/traffic.json, or None when there
-    is no record or the decode source has changed since it was taken."""
+    is no record or the kernel's source file has changed since it was taken."""
     import hashlib
 
     try:
         rec = json.load(open(path)).get(key)
     except (OSError, ValueError):
         return None
-    if not rec:
+    if not rec or not rec.get("source_file"):
         return None
-    src = os.path.join(ROOT, "paged_kv_cache_273_amd", "csrc", "decode.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("decode_source_sha256") != sha:
+    src = os.path.join(ROOT, rec["source_file"])
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
 
