@@ -454,16 +454,12 @@ hipError_t launch_prefill_t(const DecodeArgs& a, int max_query_len, bool nt, hip
         return hipErrorInvalidConfiguration;
     const size_t lds = 2 * (size_t)PCfg<D, KVF>::BUF;
     // two tile buffers exceed 64 KB at D = 128: allow the kernel that much
-    // dynamic LDS (once per instantiation; gfx950 has 160 KB per CU)
-    static const hipError_t attr = [lds] {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&prefill_kernel<D, BS, KVF, 1>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BS, KVF, 0>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        return e;
-    }();
+    // dynamic LDS (gfx950 has 160 KB per CU); set on every call, so it holds
+    // for whichever device is current (a host-side call, no GPU work)
+    const void* fn = nt ? reinterpret_cast<const void*>(&prefill_kernel<D, BS, KVF, 1>)
+                        : reinterpret_cast<const void*>(&prefill_kernel<D, BS, KVF, 0>);
+    const hipError_t attr =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess)
         return attr;
     if (nt)
