@@ -332,6 +332,31 @@ def test_balanced_shapes(orc, pkv, D, bs, G, kv, Hkv):
     assert_close(lse, rlse, "balanced lse")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("B", [100, 300])
+def test_balanced_many_sequences(orc, pkv, B, kv):
+    """Batches of 100 and 300 short ragged sequences (more units than
+    launched work-groups at 300: most ranges hold several whole units and
+    the cut records of the merge sit between them); every row against the
+    oracle."""
+    wl = make_workload("llama70b_b64_ragged1k_16k_bs32", B=B, ctx_uniform=(1, 600),
+                       max_blocks=20, kv_dtype=kv, seed=2400 + B)
+    inp = generate(wl)
+    print(f"balanced merge grids B={B} kv={kv}", flush=True)
+    if kv == "fp8":
+        kc, vc, ks, vs = fp8_group(orc, inp)
+        d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
+        kp, vp = host_appended(orc, inp, kv_dtype="fp8", k_pool=kc, v_pool=vc, ks=ks, vs=vs)
+        ref, rlse = _oracle(orc, inp, kp, vp, kv_dtype="fp8", ks=ks, vs=vs)
+    else:
+        d = DeviceInputs(inp)
+        kp, vp = host_appended(orc, inp)
+        ref, rlse = _oracle(orc, inp, kp, vp)
+    out, lse = run_balanced(pkv, d)
+    assert_close(out, ref, f"balanced B={B}")
+    assert_close(lse, rlse, f"balanced B={B} lse")
+
+
 @pytest.mark.parametrize("Hkv", [2, 8])
 def test_balanced_empty_and_ragged(orc, pkv, Hkv):
     ctx = (0, 5000, 0, 1, 33, 7000, 0, 64)

@@ -283,6 +283,23 @@ def test_verify4_fullsize_sampled(orc, pkv, kv):
         assert_close(l[row, hq], rl[0, hq], f"lse row {row} head {hq}")
 
 
+@pytest.mark.parametrize("B", [60, 300])
+def test_many_sequences(orc, pkv, B):
+    """Four new tokens per sequence over short ragged contexts, batches of 60
+    and 300 (more units than launched work-groups); every row against the
+    oracle."""
+    wl = make_workload("llama70b_b64_ragged1k_16k_bs32_verify4", B=B, ctx_uniform=(4, 500),
+                       max_blocks=16, seed=2500 + B)
+    mq = generate_multiquery(wl)
+    print(f"mq merge grids B={B}", flush=True)
+    d = MQDevice(mq)
+    out, lse = run_mq(pkv, d)
+    kp, vp = host_written(orc, mq)
+    ref, rlse = oracle_mq(orc, mq, kp, vp)
+    assert_close(out, ref, f"mq B={B}")
+    assert_close(lse, rlse, f"mq B={B} lse")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
 def test_prefill_chunk_sampled(orc, pkv, kv):
     """A 700-token chunk at the end of 3000-token prompts (8B shape): the
