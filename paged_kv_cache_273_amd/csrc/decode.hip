@@ -108,6 +108,9 @@ struct Cfg {
     // the transposing reads of the PV operands are free of bank conflicts
     static constexpr int PITCH = D * 2 + 32;
     static constexpr int LDS_BYTES = kTile * PITCH;     // per wave
+    // LDS row pitch of staged 1-byte K rows (whole-row loads): 16 bytes of
+    // padding put the 16 rows one operand read gathers on disjoint banks
+    static constexpr int KPITCH = ROW_BYTES + 16;
     static constexpr int Q_BYTES = KSTEPS * kWave * 16;  // Q operands of one column tile
     static_assert(16 % V_RPI == 0, "a V load must stay inside one 16-token block");
 };
@@ -115,11 +118,13 @@ struct Cfg {
 // LDS slice of one wave: the V staging tile, plus the Q operands when a
 // wave has several column tiles (their registers would not fit beside the
 // accumulators and the tile in flight; each lane reads back only what it
-// wrote, so the slice needs no barrier).
-template <int D, int KVF, int NCT>
+// wrote, so the slice needs no barrier), plus the K rows when they are
+// staged (KROW).
+template <int D, int KVF, int NCT, bool KROW = false>
 constexpr int wave_lds_bytes()
 {
-    return Cfg<D, KVF>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, KVF>::Q_BYTES : 0);
+    return Cfg<D, KVF>::LDS_BYTES + (NCT > 1 ? NCT * Cfg<D, KVF>::Q_BYTES : 0)
+           + (KROW ? kTile * Cfg<D, KVF>::KPITCH : 0);
 }
 
 // First of the 8 consecutive head-dim elements that lane group q feeds to
@@ -243,7 +248,8 @@ struct NoSegments {
 // emit(segment, r) takes the segment's finished state and r restarts,
 // while the next segment's first tile is already streaming in.  The last
 // segment's state is left in r as for a single range.
-template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL, typename Emit = NoSegments>
+template <int D, int BS, int KVF, int NT, int NCT, bool CAUSAL, bool KROW = false,
+          typename Emit = NoSegments>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char* lds, int b,
                                              int h, int t_begin, int t_end,
                                              const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT],
@@ -252,6 +258,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
 {
     using C = Cfg<D, KVF>;
     constexpr bool FOLD = KVF == 2 && NCT == 1;   // int8 zero points outside the MFMA
+    // KROW (fp8 decode): K is loaded like V, whole rows per lane group (one
+    // load instruction covers 8 full 128-byte rows instead of half rows of
+    // 16 tokens), staged in LDS as codes and read back in the operand layout
+    static_assert(!KROW || (KVF == 1 && NCT == 1 && !CAUSAL), "staged K rows: fp8 decode");
     const int lane = __lane_id();
     const int q4 = lane >> 4;
     const int r16 = lane & 15;
@@ -373,12 +383,33 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         return ta;
     };
     auto load_k = [&](const TileAddr& ta, Tile<D, KVF>& tl) {
+        if (KROW) {
+            static_assert(!KROW || C::V_LOADS == 2 * C::K_LOADS, "K rows fill the K registers");
+#pragma unroll
+            for (int k = 0; k < C::V_LOADS; ++k) {
+                const int p = (BS == 16 && k * C::V_RPI >= 16) ? ta.pB : ta.pA;
+                const unsigned char* blk = kc + (size_t)p * blk_stride;
+                tl.k[k / C::K_LOADS][k % C::K_LOADS] = load_kv<NT>(blk + v_off[k]);
+            }
+            return;
+        }
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             const unsigned char* blk = kc + (size_t)(tau ? ta.pB : ta.pA) * blk_stride;
 #pragma unroll
             for (int c = 0; c < C::K_LOADS; ++c)
                 tl.k[tau][c] = load_kv<NT>(blk + k_off[tau] + 64 * c);
+        }
+    };
+    // KROW: the K codes of the tile -> LDS rows (pitch KPITCH); the operand
+    // reads gather (token 16 tau + r16, 16-byte chunk q4 + 4c)
+    unsigned char* const klds = lds + C::LDS_BYTES;
+    auto stage_k = [&](const Tile<D, KVF>& tl) {
+#pragma unroll
+        for (int k = 0; k < C::V_LOADS; ++k) {
+            const int rr = k * C::V_RPI + lane / C::V_LPR;
+            *(u32x4*)(klds + rr * C::KPITCH + 16 * (lane % C::V_LPR)) =
+                tl.k[k / C::K_LOADS][k % C::K_LOADS];
         }
     };
     auto load_v = [&](const TileAddr& ta, Tile<D, KVF>& tl) {
@@ -463,7 +494,11 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
             for (int c = 0; c < C::K_LOADS; ++c) {
                 if (KVF) {
                     u32x4 lo, hi;
-                    codes_to_bf16<KVF, FOLD>(tl.k[tau][c], tau ? ta.kzB : ta.kzA, lo, hi);
+                    const u32x4 raw =
+                        KROW ? *(const u32x4*)(klds + (16 * tau + r16) * C::KPITCH
+                                               + 16 * (q4 + 4 * c))
+                             : tl.k[tau][c];
+                    codes_to_bf16<KVF, FOLD>(raw, tau ? ta.kzB : ta.kzA, lo, hi);
 #pragma unroll
                     for (int j = 0; j < NCT; ++j) {
                         sacc[j][tau] = mfma_16x16x32(as_bf16x8(lo), qop(j, 2 * c), sacc[j][tau]);
@@ -597,12 +632,17 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
         const int t0 = t_begin + kTile * it;
         const TileAddr tn = tile_addr(t0 + kTile);
         stage_v(t0, ta, tl, false);
+        if (KROW)
+            stage_k(tl);
         if (append_last && it == ntiles - 2)
             stores_before_loads();             // tile tn holds slot t_end - 1
         load_v(tn, tl);
+        if (KROW)
+            load_k(tn, tl);
         f32x4 sacc[NCT][2];
         qk(ta, tl, sacc);
-        load_k(tn, tl);
+        if (!KROW)
+            load_k(tn, tl);
         softmax_pv(t0, ta, sacc, masked);
         ta = tn;
         if (seg_tiles > 0 && (it + 1) % seg_tiles == 0) {   // a segment ends here
@@ -619,6 +659,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     {
         const int t0 = t_begin + kTile * (ntiles - 1);
         stage_v(t0, ta, tl, true);
+        if (KROW)
+            stage_k(tl);
         f32x4 sacc[NCT][2];
         qk(ta, tl, sacc);
         softmax_pv(t0, ta, sacc, true);
@@ -860,6 +902,11 @@ __device__ __forceinline__ long long range_of(long long x, long long total, long
     return r;
 }
 
+// Decode steps over fp8 caches of 32-token blocks read K as whole rows and
+// stage it in LDS (attend_range KROW).
+template <int KVF, int BS, bool MQ>
+constexpr bool kStagedKRows = KVF == 1 && BS == 32 && !MQ;
+
 // Several new tokens over a bf16 cache: at most four-wave groups at one
 // wave per SIMD, so a wave may hold 512 registers (its column tiles'
 // accumulators, the tile in flight and the softmax state spilled to
@@ -903,7 +950,10 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     int n = tiles_of(T);
     int ncg = col_groups<MQ, NCT>(a, b);
     int u = (int)((r0 - before * ngroups) / n);      // unit of b: hg * ncg + cg
-    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, KVF, NCT>();
+    // fp8 decode on 32-token blocks: K rows staged in LDS (16-token blocks:
+    // measured flat to -2.6%, the direct operand loads stay)
+    constexpr bool KROW = kStagedKRows<KVF, BS, MQ>;
+    unsigned char* lds = lds_all + wave * wave_lds_bytes<D, KVF, NCT, KROW>();
     const int rows_per_slot = HG * cpw;
     long long x = r0;
     int piece = 0;
@@ -921,7 +971,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
         const size_t slot = 2 * (size_t)wg + (piece == 0 ? 0 : 1);
         if (!MQ) {
             RangeAcc<D> acc[1];
-            attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end,
+            attend_range<D, BS, KVF, NT, 1, false, KROW>(a, lds, b, h, t_begin, t_end,
                                                    decode_cols(a, b, h, D), acc,
                                                    a.k_new != nullptr && pend == uend);
             float inv, lse;
@@ -1158,7 +1208,8 @@ int balanced_occupancy(int head_group)
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks,
             reinterpret_cast<const void*>(&decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>),
-            head_group * kWave, (size_t)head_group * wave_lds_bytes<D, KVF, NCT>())
+            head_group * kWave,
+            (size_t)head_group * wave_lds_bytes<D, KVF, NCT, kStagedKRows<KVF, BS, MQ>>())
         != hipSuccess)
         return 0;
     return blocks;
@@ -1168,7 +1219,8 @@ template <int D, int BS, int KVF, int NCT, bool MQ>
 hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt,
                              hipStream_t stream)
 {
-    const size_t lds = (size_t)ws.head_group * wave_lds_bytes<D, KVF, NCT>();
+    const size_t lds =
+        (size_t)ws.head_group * wave_lds_bytes<D, KVF, NCT, kStagedKRows<KVF, BS, MQ>>();
     const dim3 grid((unsigned)ws.ngroups_launched), block(ws.head_group * kWave);
     if (nt)
         hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>), grid, block, lds,

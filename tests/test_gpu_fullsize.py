@@ -142,3 +142,26 @@ def test_full_size_fp8_all_layers(orc, pkv):
         assert torch.equal(o_again, outs[0])
         del d
         torch.cuda.empty_cache()
+
+
+def test_full_size_70b_fp8_sampled(orc, pkv):
+    """The 70B ragged batch over an fp8 cache with a scale per (block, kv
+    head), 32-token blocks (K rows staged through LDS): the fused append +
+    balanced step the benchmark times and the plain balanced call, on 128
+    sampled rows; the appended caches bit for bit."""
+    wl = make_workload("llama70b_b64_ragged1k_16k_bs32", kv_dtype="fp8")
+    inp = generate(wl)
+    _say(f"full size 70B fp8: {inp.num_blocks} blocks, ctx sum {int(inp.context_lens.sum())}")
+    kc, vc, ks, vs = fp8_group(orc, inp)
+    d = DeviceInputs(inp, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
+    kp, vp = host_appended(orc, inp, kv_dtype="fp8", k_pool=kc, v_pool=vc, ks=ks, vs=vs)
+    fo, fl = _balanced(pkv, d, fused=True)
+    assert np.array_equal(d.k.cpu().numpy(), kp), "fp8 fused append: K differs"
+    assert np.array_equal(d.v.cpu().numpy(), vp), "fp8 fused append: V differs"
+    rows = sample_rows(wl.B, wl.Hq, 128, seed=7)
+    ref, ref_lse, rr = oracle_rows(orc, inp.query[0], kp, vp, inp.block_tables,
+                                   inp.context_lens, inp.scale, block_size=wl.block_size,
+                                   Hkv=wl.Hkv, kv_dtype="fp8", ks=ks, vs=vs, rows=rows)
+    _compare(fo, fl, ref, ref_lse, rr, "70B fp8 fused append + balanced")
+    out, lse = _balanced(pkv, d)
+    _compare(out, lse, ref, ref_lse, rr, "70B fp8 balanced")
