@@ -1061,21 +1061,26 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 }
 
 // Merge of the recorded cut units.  Work-group (r, y) takes the unit that
-// work-group r of the main launch recorded and merges kMergeWaves of its
-// rows, one wave per row (row = kv head of the group x column).  Lane
-// (p, c) owns four output elements (column c) and every npg-th piece
-// starting at p; the npg partial sums meet through lane butterflies.
-// The extra column r = R writes out = 0, lse = -inf for the rows of empty
-// sequences (decode step only: with several new tokens an empty sequence
-// has no rows).
+// work-group r of the main launch recorded and merges kMergeWaves x
+// kMergeRows of its rows (row = kv head of the group x column): each wave
+// four rows, 16 lanes per row, each lane eight output elements over every
+// piece of the unit, so no lane exchanges anything.  (One row per wave
+// launched 4x the waves, and most of them only read a record that holds
+// no cut: the launch time followed the wave count, 8.4 us for the 70B
+// batch and 23 us for its 4-token verification.)  The extra column r = R
+// writes out = 0, lse = -inf for the rows of empty sequences (decode step
+// only: with several new tokens an empty sequence has no rows).
 constexpr int kMergeWaves = 4;
+constexpr int kMergeRows = 4;      // rows per wave
 
 template <int D, int NCT, bool MQ>
 __global__ __launch_bounds__(kMergeWaves * kWave)
 void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
 {
-    constexpr int cols = D / 4;
-    constexpr int npg = kWave / cols;
+    constexpr int kLanes = kWave / kMergeRows;     // lanes per row
+    constexpr int kElems = D / kLanes;             // output elements per lane
+    constexpr int kVecs = kElems / 4;
+    static_assert(kElems % 4 == 0, "whole f32x4 per lane");
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int HG = ws.head_group;
@@ -1102,7 +1107,8 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
     const int b = rec.b;
     if (b < 0)
         return;
-    const int in_slot = blockIdx.y * kMergeWaves + wave;   // w * cpw + column
+    // w * cpw + column
+    const int in_slot = (blockIdx.y * kMergeWaves + wave) * kMergeRows + lane / kLanes;
     if (in_slot >= HG * cpw)
         return;
     const int NS = ws.head_split;
@@ -1124,7 +1130,8 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
             return;
         orow = (size_t)(rec.qs + i) * a.Hq + h * G + (col - i * G);
     }
-    float* o = a.out + orow * D;
+    const int e0 = (lane % kLanes) * kElems;         // this lane's first element
+    float* o = a.out + orow * D + e0;
     const long long total = rec.total;
     const long long R = ranges_of(ws.ngroups_launched / NS, total);
     const long long ustart = rec.ustart;
@@ -1140,30 +1147,30 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
         const long long slot = 2 * (r * NS + hs) + ((r == rf && s0 < ustart) ? 1 : 0);
         return slot * rows_per_slot + in_slot;
     };
-    const int p0 = lane / cols;
-    const int c4 = lane % cols;
-    // one online pass (running max, rescaled sums) over this lane's
-    // pieces, eight pieces' loads in flight per step
+    // one online pass (running max, rescaled sums) over the pieces, eight
+    // pieces' loads in flight per step
     constexpr int kBatch = 8;
     float m = -__builtin_inff();
     float wsum = 0.f;
-    f32x4 accv = {0.f, 0.f, 0.f, 0.f};
-    for (long long base = rf + p0; base <= rl; base += kBatch * npg) {
-        long long pr[kBatch];
+    f32x4 acc[kVecs];
+#pragma unroll
+    for (int e = 0; e < kVecs; ++e)
+        acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (long long base = rf; base <= rl; base += kBatch) {
         float l[kBatch];
-        f32x4 v[kBatch];
+        f32x4 v[kBatch][kVecs];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            const long long r = base + (long long)k * npg;
-            pr[k] = r <= rl ? piece_row(r) : -1;
-        }
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
+            const long long pr = base + k <= rl ? piece_row(base + k) : -1;
             l[k] = -__builtin_inff();
-            v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (pr[k] >= 0) {
-                l[k] = ws.part_lse[pr[k]];
-                v[k] = *(const f32x4*)(ws.part_out + pr[k] * D + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < kVecs; ++e)
+                v[k][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (pr >= 0) {
+                l[k] = ws.part_lse[pr];
+#pragma unroll
+                for (int e = 0; e < kVecs; ++e)
+                    v[k][e] = *(const f32x4*)(ws.part_out + pr * D + e0 + 4 * e);
             }
         }
         float mb = l[0];
@@ -1175,31 +1182,24 @@ void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
             continue;
         const float sc = __expf(m - m_new);
         wsum *= sc;
-        accv *= sc;
+#pragma unroll
+        for (int e = 0; e < kVecs; ++e)
+            acc[e] *= sc;
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const float wt = __expf(l[k] - m_new);
             wsum += wt;
-            accv += wt * v[k];
+#pragma unroll
+            for (int e = 0; e < kVecs; ++e)
+                acc[e] += wt * v[k][e];
         }
         m = m_new;
     }
-    // bring the npg lane groups of a column to a common max, then add them
-    const float mrow = wave_max(m);
-    const float f = __expf(m - mrow);
-    wsum *= f;
-    accv *= f;
-    m = mrow;
+    const float inv = 1.0f / wsum;
 #pragma unroll
-    for (int k = cols; k < kWave; k <<= 1) {
-        wsum += xor_shuffle(wsum, k);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            accv[e] += xor_shuffle(accv[e], k);
-    }
-    if (lane < cols)
-        *(f32x4*)(o + 4 * c4) = accv * (1.0f / wsum);
-    if (a.lse_out && lane == 0)
+    for (int e = 0; e < kVecs; ++e)
+        *(f32x4*)(o + 4 * e) = acc[e] * inv;
+    if (a.lse_out && e0 == 0)
         a.lse_out[orow] = m + __logf(wsum);
 }
 
@@ -1234,7 +1234,8 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt
     if (e != hipSuccess)
         return e;
     const int cpw = MQ ? 16 * NCT : a.G;
-    const unsigned ychunks = (unsigned)((ws.head_group * cpw + kMergeWaves - 1) / kMergeWaves);
+    const int rows_per_group = kMergeWaves * kMergeRows;
+    const unsigned ychunks = (unsigned)((ws.head_group * cpw + rows_per_group - 1) / rows_per_group);
     const dim3 mgrid((unsigned)ws.ngroups_launched + 1, ychunks);
     hipLaunchKernelGGL((balanced_merge_kernel<D, NCT, MQ>), mgrid, dim3(kMergeWaves * kWave), 0,
                        stream, a, ws);
