@@ -935,7 +935,25 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     const int G = a.G;
     constexpr int kCols = 16 * NCT;                  // MQ columns per wave
     const int cpw = MQ ? kCols : G;                  // workspace rows per wave
-    const long long total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
+    // Tiles of the call and the sequence b holding the range's first tile
+    // (with the tiles of the sequences before it).  Up to 64 sequences: one
+    // length (and query count) per lane serves the total, the search and
+    // b's length -- two dependent round trips fewer at the start of every
+    // work-group than scanning the lengths again.
+    const bool one_scan = a.B <= kWave;
+    long long incl = 0, n_l = 0;
+    int T_l = 0, ncg_l = 0;
+    long long total;
+    if (one_scan) {
+        const int lb = __lane_id();
+        T_l = lb < a.B ? a.context_lens[lb] : 0;
+        ncg_l = lb < a.B ? col_groups<MQ, NCT>(a, lb) : 0;
+        n_l = (long long)tiles_of(T_l) * ncg_l;
+        incl = MQ ? wave_inclusive_scan_ll(n_l) : (long long)wave_inclusive_scan((int)n_l);
+        total = readlane_ll(incl, kWave - 1) * ngroups;
+    } else {
+        total = tiles_before<MQ, NCT>(a, a.B) * ngroups;
+    }
     const long long R = ranges_of(ws.ngroups_launched / NS, total);
     const long long r0 = range_start(r, total, R);
     const long long r1 = range_start(r + 1, total, R);
@@ -945,12 +963,20 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
             ws.cuts[wg] = cut;
         return;
     }
-    int b;
+    int b, T, ncg;
     long long before;
-    locate_tile<MQ, NCT>(a, ngroups, r0, b, before);
-    int T = a.context_lens[b];
+    if (one_scan) {
+        // r0 < total: some lane's inclusive count passes it
+        b = __builtin_ctzll(__ballot(incl * ngroups > r0));
+        before = readlane_ll(incl - n_l, b);
+        T = __builtin_amdgcn_readlane(T_l, b);
+        ncg = __builtin_amdgcn_readlane(ncg_l, b);
+    } else {
+        locate_tile<MQ, NCT>(a, ngroups, r0, b, before);
+        T = a.context_lens[b];
+        ncg = col_groups<MQ, NCT>(a, b);
+    }
     int n = tiles_of(T);
-    int ncg = col_groups<MQ, NCT>(a, b);
     int u = (int)((r0 - before * ngroups) / n);      // unit of b: hg * ncg + cg
     // fp8 decode on 32-token blocks: K rows staged in LDS (16-token blocks:
     // measured flat to -2.6%, the direct operand loads stay)
