@@ -1089,7 +1089,7 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
 // Merge of the recorded cut units.  Work-group (r, y) takes the unit that
 // work-group r of the main launch recorded and merges kMergeWaves x
 // kMergeRows of its rows (row = kv head of the group x column): each wave
-// four rows, 16 lanes per row, each lane eight output elements over every
+// four rows, 16 lanes per row, each lane D / 16 output elements over every
 // piece of the unit, so no lane exchanges anything.  (One row per wave
 // launched 4x the waves, and most of them only read a record that holds
 // no cut: the launch time followed the wave count, 8.4 us for the 70B
