@@ -238,6 +238,13 @@ struct NoSegments {
     }
 };
 
+// The block-table entries j_first + lane (j_first: the range's first
+// block) when the caller loaded them ahead, beside the sequence length.
+struct TableWindow {
+    int entries = 0;
+    bool loaded = false;
+};
+
 // One wave attends its columns (kv head h of sequence b) over the logical
 // tokens [t_begin, t_end) (non-empty), streaming 32-token tiles.  With
 // CAUSAL, tokens at or past a column's limit are masked as well; a column
@@ -256,7 +263,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
                                              int h, int t_begin, int t_end,
                                              const Cols<NCT>& cs, RangeAcc<D> (&r)[NCT],
                                              bool append_last = false, int seg_tiles = 0,
-                                             Emit emit = Emit())
+                                             Emit emit = Emit(), TableWindow win = TableWindow())
 {
     using C = Cfg<D, KVF>;
     constexpr bool FOLD = KVF == 2 && NCT == 1;   // int8 zero points outside the MFMA
@@ -321,8 +328,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, unsigned char*
     const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
     const int j_first = t_begin / BS;
     const int j_last = (t_end - 1) / BS;
-    int tbl_base = -1;
-    int tbl = 0;
+    int tbl_base = win.loaded ? 0 : -1;
+    int tbl = win.entries;
     auto phys = [&](int j) -> int {
         int jj = min(j, j_last) - j_first;
         int base = jj & ~63;
@@ -734,6 +741,16 @@ void decode_kernel(DecodeArgs a)
     if (b >= a.B)
         return;
     const int T = a.context_lens[b];
+    // the block-table window of the wave's first tile, loaded beside the
+    // length instead of after it (entries past the live blocks are read,
+    // never dereferenced)
+    TableWindow win;
+    {
+        const long long j0 = SPLIT ? (long long)split0 * a.split_tokens / BS : 0;
+        const long long idx = j0 + __lane_id();
+        win.entries = idx < a.max_blocks ? a.block_tables[(size_t)b * a.max_blocks + idx] : 0;
+        win.loaded = true;
+    }
     const int hq = h * a.G + r16;
     const bool live_col = r16 < a.G;
     if (!SPLIT && T <= 0) {                   // empty sequence, single pass
@@ -759,7 +776,7 @@ void decode_kernel(DecodeArgs a)
     if (!SPLIT) {
         RangeAcc<D> r[1];
         attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, 0, T, decode_cols(a, b, h, D), r,
-                                               a.k_new != nullptr);
+                                               a.k_new != nullptr, 0, NoSegments(), win);
         float inv, lse;
         finish_range<D>(r[0], inv, lse);
         if (!live_col)
@@ -779,7 +796,7 @@ void decode_kernel(DecodeArgs a)
     auto emit = [&](int seg, RangeAcc<D> (&rr)[1]) { store_split(split0 + seg, rr); };
     attend_range<D, BS, KVF, NT, 1, false>(a, lds, b, h, t_begin, t_end, decode_cols(a, b, h, D),
                                            r, a.k_new != nullptr && t_end == T,
-                                           SPW > 1 ? a.split_tokens / kTile : 0, emit);
+                                           SPW > 1 ? a.split_tokens / kTile : 0, emit, win);
     store_split(split0 + (t_end - 1 - t_begin) / a.split_tokens, r);
 }
 
