@@ -51,8 +51,11 @@ MIN_TIMED_S = 0.05           # timed device work of each secondary workload
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # steady state: a short loop (50 steps, ~18 ms of device work) reads the
+    # clocks still ramping (fp8 70B batch 5.79 TB/s over 50 steps, 6.29 over
+    # 2000; steps timed one by one read the same 186 us either way)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--mode", default="auto",
                    choices=["auto", "balanced", "split", "single", "multiquery", "swap",
