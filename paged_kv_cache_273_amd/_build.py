@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-parameter",
+    # leading scalar kernel arguments arrive preloaded in SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 # the host pass does not know the device-only feature flag: drop that notice
 _NOISE = "is not a recognized feature for this target"

@@ -933,8 +933,30 @@ constexpr bool kStagedKRows = KVF == 1 && BS == 32 && !MQ;
 template <int D, int BS, int KVF, int NT, int NCT, bool MQ>
 __global__ __launch_bounds__((MQ && KVF == 0) ? kMaxMqHeadGroup * kWave : kMaxHeadGroup * kWave,
                              (MQ && KVF == 0) ? 1 : PKV_MIN_WAVES_PER_EU)
-void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
+void decode_balanced_kernel(const int32_t* pre_lens, const int32_t* pre_qstart, int32_t pre_B,
+                            int32_t pre_Hkv, int32_t pre_G, int32_t pre_groups,
+                            int32_t pre_split, int32_t pre_hg, DecodeArgs a, BalanceArgs ws)
 {
+    // the fields the schedule's first steps read, passed again as leading
+    // scalars: they arrive preloaded in SGPRs (kernel-argument preload), so
+    // the length scan is issued without a kernel-argument fetch before it
+    // first memory access of the kernel (batches of up to 64 sequences):
+    // each lane's sequence length (and query offsets), from preloaded
+    // scalars only, so nothing waits for a kernel-argument fetch before it
+    const bool one_scan = pre_B <= kWave;
+    const int lane_b = __lane_id();
+    const bool lane_live = one_scan && lane_b < pre_B;
+    const int T_first = lane_live ? pre_lens[lane_b] : 0;
+    const int qs_first = (MQ && lane_live) ? pre_qstart[lane_b] : 0;
+    const int qe_first = (MQ && lane_live) ? pre_qstart[lane_b + 1] : 0;
+    a.context_lens = pre_lens;
+    a.query_start = pre_qstart;
+    a.B = pre_B;
+    a.Hkv = pre_Hkv;
+    a.G = pre_G;
+    ws.ngroups_launched = pre_groups;
+    ws.head_split = pre_split;
+    ws.head_group = pre_hg;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_all[];  // HG slices
 
     const int q4 = __lane_id() >> 4;
@@ -957,14 +979,12 @@ void decode_balanced_kernel(DecodeArgs a, BalanceArgs ws)
     // length (and query count) per lane serves the total, the search and
     // b's length -- two dependent round trips fewer at the start of every
     // work-group than scanning the lengths again.
-    const bool one_scan = a.B <= kWave;
     long long incl = 0, n_l = 0;
     int T_l = 0, ncg_l = 0;
     long long total;
     if (one_scan) {
-        const int lb = __lane_id();
-        T_l = lb < a.B ? a.context_lens[lb] : 0;
-        ncg_l = lb < a.B ? col_groups<MQ, NCT>(a, lb) : 0;
+        T_l = T_first;
+        ncg_l = !lane_live ? 0 : MQ ? ((qe_first - qs_first) * a.G + kCols - 1) / kCols : 1;
         n_l = (long long)tiles_of(T_l) * ncg_l;
         incl = MQ ? wave_inclusive_scan_ll(n_l) : (long long)wave_inclusive_scan((int)n_l);
         total = readlane_ll(incl, kWave - 1) * ngroups;
@@ -1118,8 +1138,15 @@ constexpr int kMergeRows = 4;      // rows per wave
 
 template <int D, int NCT, bool MQ>
 __global__ __launch_bounds__(kMergeWaves * kWave)
-void balanced_merge_kernel(DecodeArgs a, BalanceArgs ws)
+void balanced_merge_kernel(const CutRecord* pre_cuts, int32_t pre_groups, int32_t pre_split,
+                           int32_t pre_hg, DecodeArgs a, BalanceArgs ws)
 {
+    // the record array and the schedule's shape arrive preloaded in SGPRs
+    // (leading scalar arguments), so the record read is issued at once
+    ws.cuts = const_cast<CutRecord*>(pre_cuts);
+    ws.ngroups_launched = pre_groups;
+    ws.head_split = pre_split;
+    ws.head_group = pre_hg;
     constexpr int kLanes = kWave / kMergeRows;     // lanes per row
     constexpr int kElems = D / kLanes;             // output elements per lane
     constexpr int kVecs = kElems / 4;
@@ -1269,10 +1296,12 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt
     const dim3 grid((unsigned)ws.ngroups_launched), block(ws.head_group * kWave);
     if (nt)
         hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 1, NCT, MQ>), grid, block, lds,
-                           stream, a, ws);
+                           stream, a.context_lens, a.query_start, a.B, a.Hkv, a.G,
+                           ws.ngroups_launched, ws.head_split, ws.head_group, a, ws);
     else
         hipLaunchKernelGGL((decode_balanced_kernel<D, BS, KVF, 0, NCT, MQ>), grid, block, lds,
-                           stream, a, ws);
+                           stream, a.context_lens, a.query_start, a.B, a.Hkv, a.G,
+                           ws.ngroups_launched, ws.head_split, ws.head_group, a, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -1281,7 +1310,8 @@ hipError_t launch_balanced_t(const DecodeArgs& a, const BalanceArgs& ws, bool nt
     const unsigned ychunks = (unsigned)((ws.head_group * cpw + rows_per_group - 1) / rows_per_group);
     const dim3 mgrid((unsigned)ws.ngroups_launched + 1, ychunks);
     hipLaunchKernelGGL((balanced_merge_kernel<D, NCT, MQ>), mgrid, dim3(kMergeWaves * kWave), 0,
-                       stream, a, ws);
+                       stream, (const CutRecord*)ws.cuts, ws.ngroups_launched, ws.head_split,
+                       ws.head_group, a, ws);
     return hipGetLastError();
 }
 
