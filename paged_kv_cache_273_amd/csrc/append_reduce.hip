@@ -84,8 +84,18 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a)
 constexpr int kReduceThreads = 256;
 constexpr int kReduceBatch = 8;
 
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a)
+__global__ __launch_bounds__(kReduceThreads)
+void reduce_kernel(const float* pre_out, const float* pre_lse, const int32_t* pre_lens,
+                   int32_t pre_Hq, int32_t pre_split_tokens, int32_t pre_max_splits, ReduceArgs a)
 {
+    // the fields of the first loads, again as leading scalars preloaded in
+    // SGPRs: the length load waits for no argument fetch
+    a.partial_out = pre_out;
+    a.partial_lse = pre_lse;
+    a.context_lens = pre_lens;
+    a.Hq = pre_Hq;
+    a.split_tokens = pre_split_tokens;
+    a.max_splits = pre_max_splits;
     __shared__ f32x4 acc_lds[kReduceThreads];
     __shared__ float m_lds[kReduceThreads];
     __shared__ float w_lds[kReduceThreads];
@@ -214,7 +224,9 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
         return hipSuccess;
     if (rows > 0x7FFFFFFFLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kReduceThreads), 0, stream, a);
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rows), dim3(kReduceThreads), 0, stream,
+                       a.partial_out, a.partial_lse, a.context_lens, a.Hq, a.split_tokens,
+                       a.max_splits, a);
     return hipGetLastError();
 }
 

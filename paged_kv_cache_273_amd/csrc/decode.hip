@@ -719,8 +719,19 @@ __device__ __forceinline__ void store_empty_row(float* o)
 // 6.0-6.8 TB/s from 2048-16384 waves).
 template <int D, int BS, int KVF, int NT, bool SPLIT, int SPW>
 __global__ __launch_bounds__(kWavesPerGroup * kWave, PKV_MIN_WAVES_PER_EU)
-void decode_kernel(DecodeArgs a)
+void decode_kernel(const int32_t* pre_lens, const int32_t* pre_tables, int32_t pre_B,
+                   int32_t pre_Hkv, int32_t pre_max_blocks, int32_t pre_max_splits,
+                   int32_t pre_split_tokens, DecodeArgs a)
 {
+    // the fields the first loads need, again as leading scalars preloaded in
+    // SGPRs: the length and block-table loads wait for no argument fetch
+    a.context_lens = pre_lens;
+    a.block_tables = pre_tables;
+    a.B = pre_B;
+    a.Hkv = pre_Hkv;
+    a.max_blocks = pre_max_blocks;
+    a.max_splits = pre_max_splits;
+    a.split_tokens = pre_split_tokens;
     using C = Cfg<D, KVF>;
     static_assert(SPW == 1 || SPLIT, "split groups only on the split partition");
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerGroup * C::LDS_BYTES];
@@ -1331,11 +1342,17 @@ hipError_t launch_fixed_t(const DecodeArgs& a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)groups), block(kWavesPerGroup * kWave);
     if (split && spw == 2)
-        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true, 2>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true, 2>), grid, block, 0, stream, a.context_lens,
+                           a.block_tables, a.B, a.Hkv, a.max_blocks, a.max_splits,
+                           a.split_tokens, a);
     else if (split)
-        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true, 1>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, true, 1>), grid, block, 0, stream, a.context_lens,
+                           a.block_tables, a.B, a.Hkv, a.max_blocks, a.max_splits,
+                           a.split_tokens, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, false, 1>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, BS, KVF, NT, false, 1>), grid, block, 0, stream, a.context_lens,
+                           a.block_tables, a.B, a.Hkv, a.max_blocks, a.max_splits,
+                           a.split_tokens, a);
     return hipGetLastError();
 }
 
